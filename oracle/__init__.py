@@ -1,0 +1,37 @@
+"""CPU oracle for causal prefill attention (BF16 and FP8 e4m3 inputs).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+product path (the HIP library and its Python binding) never imports, links or
+runs it, and shares no code with it.
+
+Page legend used in the citations below:
+
+* [P1] "Zyphra ZYFA: 1.76x FP8 FlashAttention Speedup on AMD MI355X"
+  (kongchang.com)
+* [P2] "Zyphra Says Its AMD MI355X Attention Kernel Is 1.76x Faster"
+  (fourweekmba.com)
+* [P3] "Zyphra 开源 ZYFA：面向 AMD MI355X 的 FP8 FlashAttention，最高提速 1.76 倍"
+  (attain.fans, a rendering of a MarkTechPost article)
+
+Modules:
+
+* ``attention`` -- exact causal softmax attention in fp64 (the plain
+  definition that tiled online-softmax attention reproduces, [P1] "Why prefill
+  attention deserves dedicated optimization"; the pages' own accuracy yardstick
+  is fp64 attention, [P3] "ZYFA 的 FP8 注意力有多准确？").
+* ``e4m3`` -- the OCP FP8 e4m3fn code: decode and round-to-nearest-even
+  saturating encode ([P1] "ZYFA's performance and accuracy data" describes the
+  format; [P3] "ZYFA 如何工作？" uses its integer ordering).
+* ``hadamard`` -- the 128-point Sylvester Hadamard rotation of Q and K
+  ([P3] "ZYFA 的 FP8 注意力有多准确？", [P2] "Accuracy and Code").
+* ``quantize`` -- per-(batch, head) amax/448 FP8 quantization.
+
+Every function is pinned by a ``-m "not gpu"`` test against something other than
+itself (library routines, closed forms, invariants, brute force).
+"""
+
+from .attention import attn_ref, attn_ref_rows, causal_weights_ref  # noqa: F401
+from .e4m3 import e4m3_decode, e4m3_encode_rne_sat  # noqa: F401
+from .hadamard import fwht128_f32, sylvester_hadamard  # noqa: F401
+from .quantize import quantize_ref, dequantize_ref  # noqa: F401
