@@ -1,0 +1,244 @@
+"""Benchmark: causal attention forward throughput on one MI355X.
+
+Prints ONE JSON line.  The headline workload is FP8 e4m3 causal attention at
+head dim 128 and N = 32768 (B = 1, Hq = Hkv = 32).  One step is the whole hot
+path on one batch of synthetic input already resident in HBM: the FP8 front
+end (per-head amax/448 quantization of the BF16 activations Q, K, V) followed
+by the attention kernel.  ``value`` = causal FLOPs / step time, with causal
+FLOPs = B * Hq * N^2 * (d_qk + d_v).  The BF16 point of the same metric
+(BF16, d = 128, N = 32K) is reported in the same line under ``bf16``.
+
+``roofline`` describes the attention kernel (the dominant one): its algorithmic
+FLOPs per launch divided by its average launch duration, measured with HIP
+events on the launch stream inside the timed region, against the dense MFMA
+peak of its dtype.  ``cpu_baseline`` times the CPU oracle (test
+infrastructure, untuned) on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-bf16] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd TFLOP/s (FP8 & BF16, d=128, N=32K) + % of MFMA peak"
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+PAGES_FP8_HD128_32K = 2672.0  # TFLOP/s, FP8 causal fwd, hd128, N=32K, Gaussian, on MI355X (the pages' figure)
+ATTN_KERNEL_SOURCES = ["attn_fwd.hip", "device_common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in ATTN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bf16_causal_prefill_flashattention_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, launches_bytes: float):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import bf16_causal_prefill_flashattention_amd as miattn
+    from bf16_causal_prefill_flashattention_amd.inputs import make_qkv
+
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w)
+    # inputs resident in HBM before the timed region: BF16 activations
+    q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))
+    fp8 = w.dtype == "fp8"
+    out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+    if fp8:
+        cq = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        ck = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        cv = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+        sq = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        sk = torch.empty((w.B, w.Hkv), dtype=torch.float32, device=dev)
+        sv = torch.empty((w.B, w.Hkv), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream(dev)  # every kernel below is enqueued on this stream
+
+    def step(ev=None):
+        if fp8:
+            miattn.attn_quantize_fp8(q, hadamard=w.hadamard, out=cq, scale=sq)
+            miattn.attn_quantize_fp8(k, hadamard=w.hadamard, out=ck, scale=sk)
+            miattn.attn_quantize_fp8(v, hadamard=False, out=cv, scale=sv)
+            if ev is not None:
+                ev[0].record(stream)
+            miattn.attn_fwd(cq, ck, cv, sq, sk, sv, out=out)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+            miattn.attn_fwd(q, k, v, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_ms = [a.elapsed_time(b) for a, b in events]
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    return ms_per_step, attn_ms
+
+
+def roofline(w, attn_ms):
+    flops = w.causal_flops
+    avg_s = sum(attn_ms) / len(attn_ms) * 1e-3
+    achieved = flops / avg_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {
+        "kernel": f"attn_fwd_{w.dtype}_kernel<{w.d_qk},{w.d_v}>",
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(w.name, None),
+        "avg_launch_ms": round(avg_s * 1e3, 4),
+        "min_launch_ms": round(min(attn_ms), 4),
+        "flops_per_launch": flops,
+    }
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample: whole heads, one at a
+    time, until the time budget is spent.  FP8: oracle quantization of the
+    head's Q, K, V plus exact attention on the dequantized values; BF16:
+    exact attention on the BF16 values."""
+    import numpy as np
+    import torch
+
+    from bf16_causal_prefill_flashattention_amd.inputs import make_qkv
+    from oracle import attn_ref, dequantize_ref, quantize_ref
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = make_qkv(w)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))  # the same BF16 activations the GPU step reads
+    grp = w.Hq // w.Hkv
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.Hq and (time.perf_counter() - t0) < budget_s:
+        h = done
+        g = h // grp
+        qh, kh, vh = q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1]
+        if w.dtype == "fp8":
+            cq, sq = quantize_ref(qh, w.hadamard)
+            ck, sk = quantize_ref(kh, w.hadamard)
+            cv, sv = quantize_ref(vh, False)
+            attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
+        else:
+            attn_ref(qh, kh, vh)
+        done += 1
+    el = time.perf_counter() - t0
+    flops = float(w.B) * done * float(w.N) ** 2 * (w.d_qk + w.d_v)
+    return {
+        "value": round(flops / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.Hq} query heads (all {w.N} rows each) of {w.name}, "
+                  f"{'quantize + ' if w.dtype == 'fp8' else ''}fp64 attention, {el:.1f} s",
+        "seconds": round(el, 2),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="fp8_mha_n32k")
+    ap.add_argument("--bf16-workload", default="bf16_mha_n32k")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path is a single-GPU kernel and this build has no "
+              "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = WORKLOADS[args.workload]
+    ms, attn_ms = run_gpu(w, args.steps, args.warmup)
+    value = w.causal_flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_FP8_HD128_32K, 4) if w.name == "fp8_mha_n32k" else None,
+        "dtype": "fp8_e4m3" if w.dtype == "fp8" else "bf16",
+        "data": "synthetic (seeded Gaussian N(0,1) activations, BF16 in HBM)",
+        "config": {
+            "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d_qk": w.d_qk, "d_v": w.d_v,
+            "outlier_channels": w.outliers, "hadamard": w.hadamard,
+            "step": ("quantize Q,K,V (bf16 -> e4m3, per-head amax/448) + causal attention"
+                     if w.dtype == "fp8" else "causal attention"),
+        },
+        "attn_only_tflops": round(w.causal_flops / (sum(attn_ms) / len(attn_ms) * 1e-3) / 1e12, 1),
+        "roofline": roofline(w, attn_ms),
+    }
+    if not args.no_bf16 and w.dtype == "fp8":
+        wb = WORKLOADS[args.bf16_workload]
+        msb, attn_b = run_gpu(wb, args.steps, args.warmup)
+        rec["bf16"] = {
+            "workload": wb.name,
+            "value": round(wb.causal_flops / (msb * 1e-3) / 1e12, 1),
+            "ms_per_step": round(msb, 4),
+            "roofline": roofline(wb, attn_b),
+        }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    rec["kernel_source_hash"] = kernel_source_hash()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,189 @@
+"""Causal forward (prefill) attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmiattn.so`` (declared in
+``include/miattn.h``).  It only marshals arguments: every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device memory
+and the current stream.  There is no fallback: if the library is not built, or
+a tensor is not on a GPU, the call raises.
+
+Entry points (same names as the C ABI):
+
+* ``attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None)``
+* ``attn_quantize_fp8(x, hadamard=False, out=None, scale=None)``
+* ``attn_status_string(status)``, ``attn_version()``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "attn_fwd",
+    "attn_quantize_fp8",
+    "attn_status_string",
+    "attn_version",
+    "library_path",
+    "load_library",
+    "MiattnError",
+    "DTYPE_BF16",
+    "DTYPE_FP8_E4M3",
+]
+
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3 = 1
+SRC_FP32 = 0
+SRC_BF16 = 1
+
+_LIB = None
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {attn_status_string(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmiattn.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmiattn.so (built in-tree by ``build.py``); raise if missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m bf16_causal_prefill_flashattention_amd.build`"
+        )
+    lib = ctypes.CDLL(path)
+    vp, ci, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, vp]
+    lib.attn_fwd.restype = ci
+    lib.attn_quantize_fp8.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
+    lib.attn_quantize_fp8.restype = ci
+    lib.attn_status_string.argtypes = [ci]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ci
+    _LIB = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_gpu_contig(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _as_codes(name, t):
+    torch = _torch()
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return t.view(torch.uint8)
+    raise TypeError(f"{name} must be uint8 or float8_e4m3fn codes for the FP8 path")
+
+
+def attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None):
+    """Causal attention forward.  q [B,N,Hq,d_qk], k [B,N,Hkv,d_qk],
+    v [B,N,Hkv,d_v] (contiguous BSHD, on one GPU).  BF16 tensors select the
+    BF16 path; uint8 / float8_e4m3fn codes select the FP8 path, which needs
+    fp32 scales q_scale [B,Hq], k_scale [B,Hkv], v_scale [B,Hkv].  Returns
+    ``out`` (bf16 [B,N,Hq,d_v]), allocated if not given."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu_contig(name, t)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, N, H, d]")
+    B, N, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, N, Hkv, dqk) or tuple(v.shape[:3]) != (B, N, Hkv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if q.dtype == torch.bfloat16:
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+            raise TypeError("q, k, v must share one dtype")
+        dtype = DTYPE_BF16
+        ptr_s = [None, None, None]
+    else:
+        q, k, v = _as_codes("q", q), _as_codes("k", k), _as_codes("v", v)
+        dtype = DTYPE_FP8_E4M3
+        scales = []
+        for name, s, shape in (("q_scale", q_scale, (B, Hq)), ("k_scale", k_scale, (B, Hkv)),
+                               ("v_scale", v_scale, (B, Hkv))):
+            if s is None:
+                raise ValueError(f"{name} is required for the FP8 path")
+            _check_gpu_contig(name, s)
+            if s.dtype != torch.float32 or tuple(s.shape) != shape:
+                raise ValueError(f"{name} must be float32 {shape}")
+            scales.append(s)
+        ptr_s = [s.data_ptr() for s in scales]
+    if out is None:
+        out = torch.empty((B, N, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check_gpu_contig("out", out)
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, N, Hq, dv):
+            raise ValueError("out must be bfloat16 [B, N, Hq, d_v]")
+    st = load_library().attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, N, dqk, dv, dtype,
+        ptr_s[0], ptr_s[1], ptr_s[2], _stream_handle(q.device),
+    )
+    if st != 0:
+        raise MiattnError("attn_fwd", st)
+    return out
+
+
+def attn_quantize_fp8(x, hadamard: bool = False, out=None, scale=None):
+    """Per-(batch, head) FP8 e4m3fn quantization of x [B,N,H,d] (fp32 or bf16,
+    on a GPU).  Returns (codes uint8 [B,N,H,d], scale fp32 [B,H])."""
+    torch = _torch()
+    _check_gpu_contig("x", x)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, d]")
+    if x.dtype == torch.float32:
+        src = SRC_FP32
+    elif x.dtype == torch.bfloat16:
+        src = SRC_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    B, N, H, d = x.shape
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    _check_gpu_contig("out", out)
+    _check_gpu_contig("scale", scale)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (B, N, H, d):
+        raise ValueError("out must be uint8 [B, N, H, d]")
+    if scale.dtype != torch.float32 or tuple(scale.shape) != (B, H):
+        raise ValueError("scale must be float32 [B, H]")
+    st = load_library().attn_quantize_fp8(
+        x.data_ptr(), src, out.data_ptr(), scale.data_ptr(), B, H, N, d, 1 if hadamard else 0,
+        _stream_handle(x.device),
+    )
+    if st != 0:
+        raise MiattnError("attn_quantize_fp8", st)
+    return out, scale

@@ -1,0 +1,77 @@
+"""Build libmiattn.so (the gfx950 HIP kernels plus the C ABI) in-tree with hipcc.
+
+Usage: python -m bf16_causal_prefill_flashattention_amd.build [-v]
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmiattn.so")
+SOURCES = ["attn_fwd.hip", "quantize_fp8.hip", "miattn_api.cpp"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+    # no packed fp32 math: hipcc would otherwise emit v_pk_{add,mul,fma}_f32
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmiattn.so)")
+
+
+def _compile(src: str, obj: str, verbose: bool) -> None:
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and noise not in ln]
+    if msgs and verbose:
+        print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libmiattn.so next to this file.
+    Always recompiles.  Returns the library path."""
+    with tempfile.TemporaryDirectory(prefix="miattn_build_") as tmp:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
+        out_tmp = os.path.join(tmp, "libmiattn.so")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"linking libmiattn.so failed:\n{r.stdout}\n{r.stderr}")
+        shutil.copyfile(out_tmp, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv[1:]))

@@ -1,0 +1,94 @@
+// Device-side helpers shared by the gfx950 (CDNA4) kernels of miattn.
+//
+// Vector types for the MFMA operands, thin wrappers around the matrix-core
+// builtins, LDS/global vector accesses and byte/half-word transposes.  Only
+// gfx950 is targeted; nothing here has a second code path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).
+// Lane l supplies A row (l % 32) and B column (l % 32), 8 consecutive k-slots
+// each; the k-slots of a lane are the same for A and B.  D: lane l holds column
+// (l % 32), rows 8*i + 4*(l / 32) + j in register 4*i + j.
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32 fp32) += A(32x64 e4m3) * B(64x32 e4m3), unit block scales
+// (E8M0 127 = 2^0).  Lane l supplies 32 k-slots of A row / B column (l % 32);
+// same D layout as above.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 16-byte global load that yields zeros when `valid` is false (no access).
+__device__ __forceinline__ i32x4 gload16(const void* p, bool valid) {
+  i32x4 r = {0, 0, 0, 0};
+  if (valid) r = *reinterpret_cast<const i32x4*>(p);
+  return r;
+}
+
+__device__ __forceinline__ i32x4 lds_load16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+__device__ __forceinline__ void lds_store16(void* p, i32x4 v) {
+  *reinterpret_cast<i32x4*>(p) = v;
+}
+__device__ __forceinline__ void lds_store8(void* p, i32x2 v) {
+  *reinterpret_cast<i32x2*>(p) = v;
+}
+__device__ __forceinline__ void lds_store4(void* p, int v) {
+  *reinterpret_cast<int*>(p) = v;
+}
+
+// Byte permute: result byte i = byte sel.byte[i] of the 8-byte value {hi:lo}
+// (selectors 0-3 pick from lo, 4-7 from hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Round two fp32 to bf16 (nearest-even) and pack them, first value low.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a);
+  __bf16 y = static_cast<__bf16>(b);
+  uint16_t xu = __builtin_bit_cast(uint16_t, x);
+  uint16_t yu = __builtin_bit_cast(uint16_t, y);
+  return static_cast<uint32_t>(xu) | (static_cast<uint32_t>(yu) << 16);
+}
+
+// Round four fp32 to OCP e4m3 (hardware conversion, nearest-even) and pack
+// them, first value in the low byte.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Swap with the lane 32 positions away (lane l <-> lane l ^ 32).
+__device__ __forceinline__ float xor32(float v) {
+  return __shfl_xor(v, 32, kWave);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace miattn

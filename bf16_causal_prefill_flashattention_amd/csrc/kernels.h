@@ -1,0 +1,32 @@
+// Internal (C++) interface between the C ABI layer and the HIP kernels.
+// Not exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace miattn {
+
+struct AttnParams {
+  const void* q;  // [B, N, Hq, d_qk]
+  const void* k;  // [B, N, Hkv, d_qk]
+  const void* v;  // [B, N, Hkv, d_v]
+  void* out;      // [B, N, Hq, d_v] bf16
+  const float* q_scale;  // [B, Hq]  (FP8 only)
+  const float* k_scale;  // [B, Hkv] (FP8 only)
+  const float* v_scale;  // [B, Hkv] (FP8 only)
+  int B, Hq, Hkv, N;
+  float sm_scale_log2;  // softmax scale times log2(e)
+};
+
+// Number of workgroups of one attention launch; -1 if it overflows int.
+int attn_fwd_workgroups(int B, int Hq, int N);
+
+// dtype: 0 = bf16, 1 = fp8 e4m3fn.  (d_qk, d_v) in {(128,128), (192,128)}.
+hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream);
+
+// x: [B, N, H, d] fp32 (x_dtype 0) or bf16 (x_dtype 1); x_fp8 same shape, u8;
+// scale: [B, H] fp32, also used as the amax accumulator while the call runs.
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N,
+                               int d, bool hadamard, hipStream_t stream);
+
+}  // namespace miattn

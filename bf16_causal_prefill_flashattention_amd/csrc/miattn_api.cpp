@@ -1,0 +1,108 @@
+// C ABI of libmiattn.so: host-side argument validation and dispatch to the
+// gfx950 kernels.  Declarations and the contract of every entry point are in
+// include/miattn.h.
+#include "../../include/miattn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "kernels.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_dims(int d_qk, int d_v) { return d_v == 128 && (d_qk == 128 || d_qk == 192); }
+
+// Validation touches no device state, so a rejected call enqueues nothing.
+int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+                      int d_qk, int d_v, int dtype, const float* qs, const float* ks, const float* vs) {
+  if (dtype != MIATTN_DTYPE_BF16 && dtype != MIATTN_DTYPE_FP8_E4M3) return MIATTN_ERR_DTYPE;
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return MIATTN_ERR_SIZE;
+  if (!supported_dims(d_qk, d_v)) return MIATTN_ERR_SHAPE;
+  if (B == 0 || N == 0) return MIATTN_OK;  // empty: pointers are not dereferenced
+  if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
+  if (dtype == MIATTN_DTYPE_FP8_E4M3 && (!qs || !ks || !vs)) return MIATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return MIATTN_ERR_ALIGN;
+  if (dtype == MIATTN_DTYPE_FP8_E4M3 && (!aligned(qs, 4) || !aligned(ks, 4) || !aligned(vs, 4)))
+    return MIATTN_ERR_ALIGN;
+  // every element offset must fit in 63 bits and the grid in a 31-bit count
+  const double elems = (double)B * (double)N * (double)Hq * (double)(d_qk > d_v ? d_qk : d_v);
+  if (elems > 9.0e18) return MIATTN_ERR_SIZE;
+  if ((double)B * Hq > 2147483647.0) return MIATTN_ERR_SIZE;
+  if (miattn::attn_fwd_workgroups(B, Hq, N) <= 0) return MIATTN_ERR_SIZE;
+  return MIATTN_OK;
+}
+
+int validate_quantize(const void* x, int x_dtype, void* y, float* scale, int B, int H, int N, int d,
+                      int hadamard) {
+  if (x_dtype != MIATTN_SRC_FP32 && x_dtype != MIATTN_SRC_BF16) return MIATTN_ERR_DTYPE;
+  if (hadamard != 0 && hadamard != 1) return MIATTN_ERR_DTYPE;
+  if (B < 0 || N < 0 || H < 1) return MIATTN_ERR_SIZE;
+  if (d != 128 && d != 192) return MIATTN_ERR_SHAPE;
+  if (hadamard && d != 128) return MIATTN_ERR_SHAPE;
+  if (B == 0) return MIATTN_OK;
+  if (!scale) return MIATTN_ERR_NULL;
+  if (N > 0 && (!x || !y)) return MIATTN_ERR_NULL;
+  if (!aligned(scale, 4)) return MIATTN_ERR_ALIGN;
+  if (N > 0 && (!aligned(x, 16) || !aligned(y, 16))) return MIATTN_ERR_ALIGN;
+  if ((double)B * H > 2147483647.0 / 1024.0) return MIATTN_ERR_SIZE;
+  const double blocks = (double)B * H * ((N + 255) / 256);
+  if (blocks > 2147483647.0) return MIATTN_ERR_SIZE;
+  if ((double)B * N * H * d > 9.0e18) return MIATTN_ERR_SIZE;
+  return MIATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return MIATTN_ABI_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case MIATTN_OK: return "success";
+    case MIATTN_ERR_NULL: return "a required pointer is NULL";
+    case MIATTN_ERR_SIZE: return "invalid size (negative, zero head count, Hq not a multiple of Hkv, or too large)";
+    case MIATTN_ERR_SHAPE: return "unsupported head dimensions (need (128,128) or (192,128); Hadamard needs d=128)";
+    case MIATTN_ERR_DTYPE: return "unknown dtype, source type or flag value";
+    case MIATTN_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
+    case MIATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales 4-byte alignment)";
+    default: return "unknown status code";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d_qk,
+             int d_v, int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* stream) {
+  const int st = validate_attn_fwd(q, k, v, out, B, Hq, Hkv, N, d_qk, d_v, dtype, q_scale, k_scale, v_scale);
+  if (st != MIATTN_OK || B == 0 || N == 0) return st;
+  miattn::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  // log2-domain softmax scale: tau * log2(e), tau = 1/sqrt(d_qk)
+  p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_qk));
+  const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,
+                      int hadamard, void* stream) {
+  const int st = validate_quantize(x, x_dtype, x_fp8, scale, B, H, N, d, hadamard);
+  if (st != MIATTN_OK || B == 0) return st;
+  const hipError_t e =
+      miattn::launch_quantize_fp8(x, x_dtype, x_fp8, scale, B, H, N, d, hadamard != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+/* miattn -- causal forward (prefill) attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmiattn.so.  Plain pointers and sizes only; every device pointer
+ * is a HIP device address owned by the caller.  The library never allocates,
+ * frees or synchronises: all work is enqueued on the caller's stream and the
+ * calls return as soon as it is enqueued.  Arguments are validated on the host
+ * before anything is enqueued, so a call that returns an error has launched
+ * nothing.  No C++ exception crosses this interface.  The library keeps no
+ * mutable global state; calls are reentrant.
+ *
+ * Page legend for the citations:
+ *   [P1] "Zyphra ZYFA: 1.76x FP8 FlashAttention Speedup on AMD MI355X"
+ *   [P2] "Zyphra Says Its AMD MI355X Attention Kernel Is 1.76x Faster"
+ *   [P3] "Zyphra 开源 ZYFA：面向 AMD MI355X 的 FP8 FlashAttention，最高提速 1.76 倍"
+ */
+#ifndef MIATTN_H_
+#define MIATTN_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIATTN_ABI_VERSION 1
+
+/* Element types of Q, K, V. */
+#define MIATTN_DTYPE_BF16 0     /* bfloat16 */
+#define MIATTN_DTYPE_FP8_E4M3 1 /* OCP FP8 e4m3fn codes, one byte each, with fp32 scales */
+
+/* Element types accepted by attn_quantize_fp8. */
+#define MIATTN_SRC_FP32 0
+#define MIATTN_SRC_BF16 1
+
+/* Status codes (0 = success, negative = error; nothing was enqueued). */
+#define MIATTN_OK 0
+#define MIATTN_ERR_NULL (-1)     /* a required pointer is NULL */
+#define MIATTN_ERR_SIZE (-2)     /* a size is negative, zero where it may not be, Hq % Hkv != 0, or too large */
+#define MIATTN_ERR_SHAPE (-3)    /* unsupported head dimensions, or Hadamard with d != 128 */
+#define MIATTN_ERR_DTYPE (-4)    /* unknown dtype / source type code, or a flag outside {0, 1} */
+#define MIATTN_ERR_HIP (-5)      /* the HIP runtime reported an error when enqueuing */
+#define MIATTN_ERR_ALIGN (-6)    /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
+
+/* Causal forward attention, O = softmax(tau * Q K^T + causal mask) V.
+ *
+ * Defines: the causal forward (prefill) attention pass in BF16 and FP8 e4m3
+ * with FP32 accumulation ([P2] "What Zyphra Reported"; [P3] "TL;DR"),
+ * computed tile by tile with an online softmax so the N x N score matrix is
+ * never stored ([P1] "Why prefill attention deserves dedicated
+ * optimization"); head dim 128 (with grouped-query attention) and the
+ * multi-head-latent shape d_qk = 192, d_v = 128 ([P2] "What Zyphra Reported").
+ *
+ * Layout: every tensor is contiguous [batch, sequence, head, channel] (BSHD):
+ *   q   [B, N, Hq,  d_qk]  dtype
+ *   k   [B, N, Hkv, d_qk]  dtype
+ *   v   [B, N, Hkv, d_v]   dtype
+ *   out [B, N, Hq,  d_v]   bfloat16 (written)
+ * Query i attends to keys j <= i (queries and keys share positions 0..N-1).
+ * Query head h reads key/value head h / (Hq / Hkv) (integer division).
+ * Softmax scale tau = 1 / sqrt(d_qk).
+ *
+ * dtype = MIATTN_DTYPE_FP8_E4M3: q, k, v hold e4m3fn codes and the real input
+ * is code * scale with one fp32 scale per (batch, head):
+ *   q_scale [B, Hq], k_scale [B, Hkv], v_scale [B, Hkv]   (device memory)
+ * The scales are folded into the scores before the softmax and into the
+ * output; probabilities are rounded to e4m3 for the P.V product.
+ * dtype = MIATTN_DTYPE_BF16: the scale pointers are ignored and may be NULL.
+ *
+ * Sizes: B >= 0, N >= 0 (B == 0 or N == 0 is an empty call: success, nothing
+ * enqueued), Hq >= 1, Hkv >= 1, Hq % Hkv == 0, (d_qk, d_v) in
+ * {(128, 128), (192, 128)}.  Any N is accepted (ragged tails are masked).
+ * stream: a hipStream_t, or NULL for the default stream.
+ * The result is bitwise reproducible from launch to launch (no atomics, fixed
+ * reduction order).
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d_qk,
+             int d_v, int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* stream);
+
+/* Per-(batch, head) FP8 e4m3fn quantization, the front end of the FP8 path.
+ *
+ * Defines: per-head scale factors that bring activations into the e4m3 range
+ * ([P1] "ZYFA's performance and accuracy data"), scale = amax / 448; with
+ * hadamard = 1 a 128-point Hadamard rotation of the channel dimension first,
+ * which the pages apply to Q and K to cut quantization error ([P3] "ZYFA 的
+ * FP8 注意力有多准确？"; [P2] "Accuracy and Code").
+ *
+ * x      [B, N, H, d] contiguous, fp32 (x_dtype = MIATTN_SRC_FP32) or bf16
+ *        (MIATTN_SRC_BF16), read only.
+ * x_fp8  [B, N, H, d] contiguous uint8, written with the e4m3fn codes.
+ * scale  [B, H] fp32, written with the per-(batch, head) scale; it is also used
+ *        as the amax accumulator while the call's kernels run, so it must not
+ *        alias x or x_fp8.
+ * Steps, each in fp32: y = x (or the unnormalised Sylvester transform x H_128
+ * with butterfly stages of width 1, 2, ..., 64 when hadamard = 1);
+ * amax = max |y| over the (b, h) slice; inv = 448 / amax; code =
+ * round-to-nearest-even e4m3(clamp(y * inv, -448, 448)); scale = amax / 448,
+ * times fp32(2^-3.5) when hadamard = 1 (the 1/sqrt(128) normalisation).
+ * amax == 0 gives inv = 1, scale = 1 (times fp32(2^-3.5) with hadamard), all
+ * codes 0.  The dequantized value code * scale is what attn_fwd consumes.
+ * Sizes: B >= 0, N >= 0, H >= 1, d in {128, 192}; hadamard in {0, 1} and
+ * hadamard = 1 requires d = 128.  B == 0 is an empty call; N == 0 writes the
+ * scales only.  Deterministic.  Returns MIATTN_OK or MIATTN_ERR_*. */
+int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,
+                      int hadamard, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* MIATTN_ABI_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H_ */

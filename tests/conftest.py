@@ -27,3 +27,13 @@ def gpu_available() -> bool:
 def require_gpu():
     if not gpu_available():
         pytest.skip("no GPU visible")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr before it runs, so a run that dies inside a
+    kernel still says which case it was."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

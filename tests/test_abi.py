@@ -1,0 +1,102 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/miattn.h declares, and rejects invalid arguments before touching the
+device (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bf16_causal_prefill_flashattention_amd as pkg
+
+pytestmark = pytest.mark.cpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+
+
+def header_constant(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkg.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    assert sorted(declared_functions()) == sorted(
+        ["attn_fwd", "attn_quantize_fp8", "attn_status_string", "attn_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pkg.library_path()], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_version_and_status_strings(lib):
+    assert pkg.attn_version() == header_constant("MIATTN_ABI_VERSION")
+    for code in range(-6, 1):
+        s = pkg.attn_status_string(code)
+        assert s and s != "unknown status code"
+    assert pkg.attn_status_string(-99) == "unknown status code"
+
+
+OK = 0
+E_NULL, E_SIZE, E_SHAPE, E_DTYPE, E_HIP, E_ALIGN = -1, -2, -3, -4, -5, -6
+P = 1 << 20  # a 16-byte-aligned stand-in address; never dereferenced on these paths
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, N=8, dqk=128, dv=128, dtype=0, qs=P, ks=P, vs=P):
+    return lib.attn_fwd(q, k, v, o, B, Hq, Hkv, N, dqk, dv, dtype, qs, ks, vs, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), E_NULL), (dict(k=None), E_NULL), (dict(v=None), E_NULL), (dict(o=None), E_NULL),
+    (dict(dtype=1, qs=None), E_NULL), (dict(dtype=1, vs=None), E_NULL),
+    (dict(B=-1), E_SIZE), (dict(N=-5), E_SIZE), (dict(Hq=0), E_SIZE), (dict(Hkv=0), E_SIZE),
+    (dict(Hq=6, Hkv=4), E_SIZE),
+    (dict(dqk=64, dv=64), E_SHAPE), (dict(dqk=128, dv=192), E_SHAPE), (dict(dqk=256, dv=128), E_SHAPE),
+    (dict(dtype=2), E_DTYPE), (dict(dtype=-1), E_DTYPE),
+    (dict(q=P + 8), E_ALIGN), (dict(o=P + 2), E_ALIGN), (dict(dtype=1, ks=P + 2), E_ALIGN),
+    (dict(N=0), OK), (dict(B=0), OK), (dict(N=0, q=None, k=None, v=None, o=None), OK),
+])
+def test_attn_fwd_validation(lib, kw, expect):
+    assert fwd(lib, **kw) == expect
+
+
+def quant(lib, x=P, src=0, y=P, s=P, B=1, H=2, N=8, d=128, had=0):
+    return lib.attn_quantize_fp8(x, src, y, s, B, H, N, d, had, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), E_NULL), (dict(y=None), E_NULL), (dict(s=None), E_NULL),
+    (dict(src=2), E_DTYPE), (dict(had=2), E_DTYPE),
+    (dict(B=-1), E_SIZE), (dict(H=0), E_SIZE), (dict(N=-1), E_SIZE),
+    (dict(d=64), E_SHAPE), (dict(d=192, had=1), E_SHAPE),
+    (dict(x=P + 4), E_ALIGN), (dict(s=P + 1), E_ALIGN),
+    (dict(B=0), OK),
+])
+def test_quantize_validation(lib, kw, expect):
+    assert quant(lib, **kw) == expect
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        pkg.attn_quantize_fp8(q.float())

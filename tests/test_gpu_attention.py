@@ -1,0 +1,254 @@
+"""GPU attention (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element; the full-size workloads run in the
+same launch configuration the benchmark times and compare sampled rows of
+sampled heads, which the oracle computes one by one.  BF16: relative Frobenius
+error <= 1e-2 against the oracle on the BF16 inputs.  FP8: the GPU quantizer's
+codes and scales must equal the oracle quantizer's bit for bit, and the
+attention output must be within 6e-2 of the oracle on the dequantized inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bf16_causal_prefill_flashattention_amd as miattn
+from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS, Workload, make_inputs, make_qkv
+from oracle import attn_ref, attn_ref_rows, dequantize_ref, e4m3_decode, quantize_ref
+from parity_util import TOL, per_head_rel_fro, rel_fro, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_case(w: Workload):
+    q, k, v = make_inputs(w)
+    out = miattn.attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    return out.cpu(), (q, k, v)
+
+
+def _fp8_gpu(q, k, v, hadamard):
+    cq, sq = miattn.attn_quantize_fp8(q.cuda(), hadamard=hadamard)
+    ck, sk = miattn.attn_quantize_fp8(k.cuda(), hadamard=hadamard)
+    cv, sv = miattn.attn_quantize_fp8(v.cuda(), hadamard=False)
+    out = miattn.attn_fwd(cq, ck, cv, sq, sk, sv)
+    torch.cuda.synchronize()
+    return out.cpu(), (cq.cpu().numpy(), sq.cpu().numpy(), ck.cpu().numpy(), sk.cpu().numpy(),
+                       cv.cpu().numpy(), sv.cpu().numpy())
+
+
+def _fp8_oracle_inputs(q, k, v, hadamard):
+    cq, sq = quantize_ref(q, hadamard)
+    ck, sk = quantize_ref(k, hadamard)
+    cv, sv = quantize_ref(v, False)
+    return (cq, sq, ck, sk, cv, sv)
+
+
+def _assert_same_codes(gpu, ref):
+    names = ["q codes", "q scale", "k codes", "k scale", "v codes", "v scale"]
+    for name, a, b in zip(names, gpu, ref):
+        if a.dtype == np.float32:
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+        else:
+            assert np.array_equal(a, b), f"{name}: {np.count_nonzero(a != b)} differ"
+
+
+SMALL = [
+    # (B, N, Hq, Hkv, d_qk, outliers)
+    (1, 512, 2, 2, 128, 0),  # the small exact-check workload
+    (2, 1, 2, 1, 128, 0),
+    (1, 17, 4, 2, 128, 0),
+    (1, 127, 2, 2, 128, 0),
+    (1, 129, 2, 2, 128, 0),
+    (1, 300, 8, 2, 128, 0),
+    (2, 700, 4, 4, 128, 0),
+    (1, 1024, 8, 2, 128, 4),  # GQA with activation-like outlier channels
+    (1, 333, 2, 2, 192, 0),  # MLA shape, ragged
+    (1, 1000, 4, 4, 192, 0),
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,dqk,outl", SMALL)
+def test_bf16_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl):
+    w = Workload("t", "bf16", B, Hq, Hkv, N, dqk, 128, outliers=outl, seed=N + Hq)
+    out, (q, k, v) = _bf16_case(w)
+    ref = attn_ref(q, k, v)
+    err = rel_fro(out, ref)
+    assert err <= TOL["bf16"], (err, per_head_rel_fro(out, ref))
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,dqk,outl", SMALL)
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_fp8_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl, hadamard):
+    if hadamard and dqk != 128:
+        pytest.skip("the Hadamard rotation is defined for d = 128")
+    w = Workload("t", "fp8", B, Hq, Hkv, N, dqk, 128, outliers=outl, seed=N + Hq + 1)
+    q, k, v = make_qkv(w)
+    out, gpu_codes = _fp8_gpu(q, k, v, hadamard)
+    ref_codes = _fp8_oracle_inputs(q, k, v, hadamard)
+    _assert_same_codes(gpu_codes, ref_codes)
+    cq, sq, ck, sk, cv, sv = ref_codes
+    ref = attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
+    err = rel_fro(out, ref)
+    assert err <= TOL["fp8"], (err, per_head_rel_fro(out, ref))
+
+
+def _heads_to_sample(w: Workload):
+    grp = w.Hq // w.Hkv
+    hs = {0, w.Hq - 1, (w.Hq // 2) | 1}
+    if grp > 1:
+        hs.add(grp)  # the first head of the second kv group
+    return sorted(h for h in hs if h < w.Hq)
+
+
+FULL = [("bf16_gqa_n16k", "bf16"), ("bf16_mha_n32k", "bf16"), ("fp8_mha_n1k", "fp32"), ("fp8_mha_n4k", "fp32"),
+        ("fp8_mha_n16k", "fp32"), ("fp8_mha_n32k", "fp32"), ("fp8_mha_n32k", "bf16"), ("fp8_gqa_n16k", "fp32"),
+        ("fp8_gqa_n16k_had", "fp32"), ("fp8_mla_n32k", "fp32")]
+
+
+@pytest.mark.parametrize("name,src", FULL)
+def test_full_size_sampled_rows(require_gpu, name, src):
+    """src: element type of the activations the FP8 front end reads (the
+    benchmark's step quantizes BF16 activations)."""
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    if src == "bf16":
+        q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    rows = sample_rows(w.N, 48, seed=len(name))
+    grp = w.Hq // w.Hkv
+    if w.dtype == "bf16":
+        out = miattn.attn_fwd(q.cuda(), k.cuda(), v.cuda())
+        torch.cuda.synchronize()
+        out = out.cpu()
+        errs = []
+        for h in _heads_to_sample(w):
+            g = h // grp
+            ref = attn_ref_rows(q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1], rows)
+            errs.append(rel_fro(out[:, rows, h:h + 1], ref))
+        assert max(errs) <= TOL["bf16"], errs
+        return
+    cq, sq = miattn.attn_quantize_fp8(q.cuda(), hadamard=w.hadamard)
+    ck, sk = miattn.attn_quantize_fp8(k.cuda(), hadamard=w.hadamard)
+    cv, sv = miattn.attn_quantize_fp8(v.cuda())
+    out = miattn.attn_fwd(cq, ck, cv, sq, sk, sv)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    errs = []
+    for h in _heads_to_sample(w):
+        g = h // grp
+        rq, rsq = quantize_ref(q[:, :, h:h + 1], w.hadamard)
+        rk, rsk = quantize_ref(k[:, :, g:g + 1], w.hadamard)
+        rv, rsv = quantize_ref(v[:, :, g:g + 1], False)
+        assert np.array_equal(cq[:, :, h:h + 1].cpu().numpy(), rq)
+        assert np.array_equal(ck[:, :, g:g + 1].cpu().numpy(), rk)
+        assert np.array_equal(cv[:, :, g:g + 1].cpu().numpy(), rv)
+        assert sq[:, h].cpu().numpy().view(np.uint32)[0] == rsq.view(np.uint32)[0, 0]
+        assert sk[:, g].cpu().numpy().view(np.uint32)[0] == rsk.view(np.uint32)[0, 0]
+        assert sv[:, g].cpu().numpy().view(np.uint32)[0] == rsv.view(np.uint32)[0, 0]
+        ref = attn_ref_rows(dequantize_ref(rq, rsq), dequantize_ref(rk, rsk), dequantize_ref(rv, rsv), rows)
+        errs.append(rel_fro(out[:, rows, h:h + 1], ref))
+    assert max(errs) <= TOL["fp8"], errs
+
+
+# ---------------------------------------------------------------- special cases
+
+
+def test_bf16_row_zero_is_v0_exactly(require_gpu):
+    w = Workload("t", "bf16", 2, 4, 2, 200, 128, 128, seed=3)
+    out, (q, k, v) = _bf16_case(w)
+    for h in range(4):
+        assert torch.equal(out[:, 0, h], v[:, 0, h // 2])
+
+
+def test_fp8_row_zero_is_dequantized_v0(require_gpu):
+    w = Workload("t", "fp8", 1, 4, 2, 300, 128, 128, seed=4)
+    q, k, v = make_qkv(w)
+    out, codes = _fp8_gpu(q, k, v, False)
+    cv, sv = codes[4], codes[5]
+    expect = torch.from_numpy(dequantize_ref(cv, sv)[:, 0]).to(torch.bfloat16)
+    for h in range(4):
+        a = out[:, 0, h].float()
+        b = expect[:, h // 2].float()
+        assert torch.all((a - b).abs() <= b.abs() * 2.0 ** -7 + 1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_zero_queries_give_prefix_mean(require_gpu, dtype):
+    N = 600
+    w = Workload("t", dtype, 1, 2, 1, N, 128, 128, seed=5)
+    q, k, v = make_qkv(w)
+    q.zero_()
+    if dtype == "bf16":
+        out = miattn.attn_fwd(q.bfloat16().cuda(), k.bfloat16().cuda(), v.bfloat16().cuda()).cpu()
+        vv = v.bfloat16().double().numpy()
+    else:
+        out, codes = _fp8_gpu(q, k, v, False)
+        vv = dequantize_ref(codes[4], codes[5])
+    prefix = np.cumsum(vv[0, :, 0], axis=0) / np.arange(1, N + 1)[:, None]
+    for h in range(2):
+        err = rel_fro(out[0, :, h], prefix)
+        assert err <= 4e-3, err  # equal scores: every weight is exact, only the output rounding remains
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_key_permutation_inside_window(require_gpu, dtype):
+    N, kk = 400, 150
+    w = Workload("t", dtype, 1, 2, 2, N, 128, 128, seed=6)
+    q, k, v = make_qkv(w)
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(kk + 1))
+    k2, v2 = k.clone(), v.clone()
+    k2[:, : kk + 1] = k[:, perm]
+    v2[:, : kk + 1] = v[:, perm]
+    if dtype == "bf16":
+        a = miattn.attn_fwd(q.bfloat16().cuda(), k.bfloat16().cuda(), v.bfloat16().cuda()).cpu()
+        b = miattn.attn_fwd(q.bfloat16().cuda(), k2.bfloat16().cuda(), v2.bfloat16().cuda()).cpu()
+        tol = 2 * TOL["bf16"]
+    else:
+        a, _ = _fp8_gpu(q, k, v, False)
+        b, _ = _fp8_gpu(q, k2, v2, False)  # permuting rows leaves the per-head amax unchanged
+        tol = 2 * TOL["fp8"]
+    assert rel_fro(b[:, kk:], a[:, kk:].double().numpy()) <= tol
+
+
+@pytest.mark.parametrize("dtype,dqk", [("bf16", 128), ("fp8", 128), ("fp8", 192)])
+def test_bitwise_deterministic_100_launches(require_gpu, dtype, dqk):
+    w = Workload("t", dtype, 1, 8, 2, 2048, dqk, 128, outliers=0, seed=8)
+    q, k, v = make_inputs(w)
+    if dtype == "bf16":
+        args = (q.cuda(), k.cuda(), v.cuda())
+    else:
+        cq, sq = miattn.attn_quantize_fp8(q.cuda())
+        ck, sk = miattn.attn_quantize_fp8(k.cuda())
+        cv, sv = miattn.attn_quantize_fp8(v.cuda())
+        args = (cq, ck, cv, sq, sk, sv)
+    first = miattn.attn_fwd(*args).view(torch.int16).clone()
+    out = torch.empty_like(first).view(torch.bfloat16)
+    for _ in range(100):
+        miattn.attn_fwd(*args, out=out)
+        assert torch.equal(out.view(torch.int16), first)
+
+
+def test_output_written_only_inside_bounds(require_gpu):
+    w = Workload("t", "bf16", 1, 2, 2, 77, 128, 128, seed=9)
+    q, k, v = make_inputs(w)
+    n = 77 * 2 * 128
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[2048: 2048 + n].view(1, 77, 2, 128)
+    miattn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:2048] == 7.0) and torch.all(buf[2048 + n:] == 7.0)
+
+
+def test_empty_sequence_is_a_no_op(require_gpu):
+    q = torch.empty(1, 0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    out = miattn.attn_fwd(q, q, q)
+    assert out.shape == (1, 0, 2, 128)
+
+
+def test_misaligned_pointer_is_rejected(require_gpu):
+    base = torch.zeros(1 * 16 * 2 * 128 + 1, dtype=torch.bfloat16, device="cuda")
+    q = base[1:].view(1, 16, 2, 128)
+    with pytest.raises(miattn.MiattnError) as ei:
+        miattn.attn_fwd(q, q, q)
+    assert ei.value.status == -6
