@@ -19,6 +19,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Note on bit casts: with this toolchain, __builtin_bit_cast applied to an
+// element of an ext_vector_type value (bit_cast<float>(v[i])) has been seen to
+// fold every element to v[0].  Bit-cast whole vectors, or copy the element to a
+// scalar first.
+
 // D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).
 // Lane l supplies A row (l % 32) and B column (l % 32), 8 consecutive k-slots
 // each; the k-slots of a lane are the same for A and B.  D: lane l holds column

@@ -40,11 +40,13 @@ __device__ __forceinline__ void load8(const T* src, bool valid, float v[8]);
 
 template <>
 __device__ __forceinline__ void load8<float>(const float* src, bool valid, float v[8]) {
-  i32x4 a = gload16(src, valid), b = gload16(src + 4, valid);
+  // whole-vector bit casts only (see the note on bit casts in device_common.hpp)
+  const f32x4 a = __builtin_bit_cast(f32x4, gload16(src, valid));
+  const f32x4 b = __builtin_bit_cast(f32x4, gload16(src + 4, valid));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[i] = __builtin_bit_cast(float, a[i]);
-    v[4 + i] = __builtin_bit_cast(float, b[i]);
+    v[i] = a[i];
+    v[4 + i] = b[i];
   }
 }
 
@@ -53,7 +55,7 @@ __device__ __forceinline__ void load8<__bf16>(const __bf16* src, bool valid, flo
   i32x4 a = gload16(src, valid);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t w = (uint32_t)a[i];
+    const uint32_t w = static_cast<uint32_t>(static_cast<int>(a[i]));
     v[2 * i] = __builtin_bit_cast(float, w << 16);
     v[2 * i + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
   }
