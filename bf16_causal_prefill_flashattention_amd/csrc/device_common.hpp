@@ -39,6 +39,21 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), unit block scales.  Lane l
+// supplies 32 k-slots of A row / B column (l % 16); lane group l / 16 selects
+// which quarter of the 128 k-slots.  D: lane l holds column (l % 16), rows
+// 4*(l / 16) + j in register j.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.x * b.x + a.y * b.y + c with bf16 products accumulated in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -51,6 +66,22 @@ __device__ __forceinline__ i32x4 gload16(const void* p, bool valid) {
   i32x4 r = {0, 0, 0, 0};
   if (valid) r = *reinterpret_cast<const i32x4*>(p);
   return r;
+}
+
+// Raw buffer resource over [base, base + bytes): 16-byte loads whose offset is
+// at or beyond `bytes` return zeros without touching memory, so ragged tiles
+// need no branches.  Offsets are 32-bit, so callers rebase per tile.
+// The base and size must be wave-uniform; readfirstlane states that to the
+// compiler (a descriptor it believes divergent is built in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ i32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
 }
 
 __device__ __forceinline__ i32x4 lds_load16(const void* p) {

@@ -32,6 +32,8 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, in
   const double elems = (double)B * (double)N * (double)Hq * (double)(d_qk > d_v ? d_qk : d_v);
   if (elems > 9.0e18) return MIATTN_ERR_SIZE;
   if ((double)B * Hq > 2147483647.0) return MIATTN_ERR_SIZE;
+  // kernels address one 128-key tile of K or V with 32-bit offsets
+  if ((double)Hkv * (d_qk > d_v ? d_qk : d_v) * 2.0 * 128.0 > 2147483647.0) return MIATTN_ERR_SIZE;
   if (miattn::attn_fwd_workgroups(B, Hq, N) <= 0) return MIATTN_ERR_SIZE;
   return MIATTN_OK;
 }
