@@ -40,9 +40,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmiattn.so)")
 
 
+# Per-source flags.  The attention kernel never sees NaN inputs (scores are
+# finite or -inf), so fmax needs no NaN quieting; the quantizer keeps strict IEEE.
+EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, obj: str, verbose: bool) -> None:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -12,26 +12,38 @@
 // [P3] "为什么 FP8 注意力在 MI355X 上表现不佳？").  Output is BF16.
 //
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
-// (batch, query head); each wave owns 32 queries, and two waves share each
-// SIMD.  The workgroup walks key tiles (64 keys for BF16, 128 for FP8) from key
-// 0 up to its last query; the causal mask is applied only on the tiles that
-// cross the diagonal, and a wave skips the tiles wholly above its queries.
+// (batch, query head); each wave owns 32 queries.  Key tiles hold 128 keys
+// (FP8) or 64 keys (BF16); a wave skips the tiles wholly above its queries and
+// masks only the tiles that cross its diagonal.
 //
 // Matrix layout.  A wave computes S^T = K_tile * Q^T (keys on MFMA rows,
-// queries on MFMA columns), so lane l owns query (l % 32) and holds that
-// query's scores for half of the tile's keys; the other half sits in lane
-// l ^ 32.  Row max stays inside a lane plus one exchange with lane l ^ 32.  The
-// output is accumulated transposed, O^T += V^T * P^T, so probabilities leave
-// the S^T accumulator straight into the MFMA B operand, and V^T is read from a
-// transposed LDS copy of the V tile whose key order matches the k-slots.
+// queries on MFMA columns), so lane l owns query (l % 32) and holds half of the
+// tile's scores for it; the other half sits in lane l ^ 32.  The output is
+// accumulated transposed, O^T += V^T * P^T: the probabilities leave the S^T
+// accumulator straight into the MFMA B operand, in an order of keys that the
+// V^T operand reproduces when it is read from LDS.
 //
-// Pipeline.  K/V tiles stream HBM/L2 -> registers -> LDS through two LDS
-// stages with one barrier per tile: while tile j is consumed, tile j+1 is
-// written to the other stage and tile j+2 is in flight in registers (waves 0-3
-// stage V, waves 4-7 stage K).  The two waves of a SIMD run the same
-// S -> softmax -> P.V sequence; while one turns scores into probabilities on
-// the vector ALU, the other's matrix instructions keep the matrix core busy,
-// the two-wave overlap the pages describe ([P3] "ZYFA 如何工作？").
+// Two-group ping-pong.  The matrix core and the vector ALU of a SIMD only run
+// at the same time for instructions of different waves: a wave's own softmax
+// work does not overlap its own matrix instructions.  So the 8 waves form two
+// groups (waves 0-3 and 4-7, one wave of each per SIMD) that run the same loop
+// one phase apart, separated by workgroup barriers:
+//   phase 2p   : group A matrix work  | group B vector work
+//   phase 2p+1 : group A vector work  | group B matrix work
+// where "matrix work" of step p is P_{p-1} V_{p-1} followed by S_p = K_p Q^T,
+// and "vector work" of step p is the online softmax of S_p.  This is the
+// two-wave overlap the pages describe ([P3] "ZYFA 如何工作？"), ordered here by
+// barriers instead of per-instruction scheduling.
+//
+// Data movement.  K and V tiles go from HBM/L2 straight into LDS with buffer
+// loads that write LDS (no register staging): K rows are stored with a 16-byte
+// pad so that the 32 rows one MFMA operand read touches fall in distinct LDS
+// banks; V rows are stored as they are in memory with an XOR swizzle of their
+// 16-byte chunks, and the V^T operand is read with the transposing LDS reads of
+// gfx950.  Two LDS buffers each for K and V; the loads of phase 2p are waited
+// for at the end of phase 2p+1.  Rows at or beyond N load as zeros (buffer
+// bounds), so a ragged last tile needs no branches; keys >= N lie above the
+// diagonal of every valid query and are masked.
 //
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
@@ -52,33 +64,33 @@ namespace miattn {
 namespace {
 
 constexpr int kThreads = 512;  // 8 waves, two per SIMD
-constexpr int kHalf = kThreads / 2;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
-constexpr int kStages = 2;
 
 template <bool FP8, int DQK, int DV>
 struct Cfg {
-  static constexpr int EB = FP8 ? 1 : 2;      // bytes per element
-  static constexpr int BN = FP8 ? 128 : 64;   // keys per tile
-  static constexpr int NBLK = BN / 32;        // 32-key MFMA blocks per tile
-  static constexpr int KROW = DQK * EB;       // bytes of one K row
-  static constexpr int K_STRIDE = KROW + 16;  // LDS row pitch; +16 keeps b128 reads conflict-free
-  static constexpr int VT_STRIDE = BN * EB + 16;
-  static constexpr int K_BYTES = BN * K_STRIDE;
-  static constexpr int VT_BYTES = DV * VT_STRIDE;
-  static constexpr int STAGE_BYTES = K_BYTES + VT_BYTES;
-  static constexpr int KCH = KROW / 16;                // 16-byte chunks per K row
-  static constexpr int K_TPR = kHalf / BN;             // K-staging threads per K row
-  static constexpr int K_LOADS = KCH / K_TPR;          // consecutive chunks per K-staging thread
-  static constexpr int VCH = DV * EB / 16;             // 16-byte channel chunks per V row
-  static constexpr int NREG = K_LOADS > 4 ? K_LOADS : 4;
+  static constexpr int EB = FP8 ? 1 : 2;     // bytes per element
+  static constexpr int BN = FP8 ? 128 : 64;  // keys per tile
+  static constexpr int NBLK = BN / 32;       // 32-key MFMA blocks per tile
+  static constexpr int KROW = DQK * EB;      // bytes of one K row
+  static constexpr int VROW = DV * EB;       // bytes of one V row
+  static constexpr int KCH = KROW / 16;      // 16-byte chunks per K row
+  static constexpr int VCH = VROW / 16;      // 16-byte chunks per V row
+  static constexpr int KPITCH = KROW + 16;   // padded LDS pitch of a K row
+  static constexpr int K_TILE = BN * KPITCH;
+  static constexpr int V_TILE = BN * VROW;
+  static constexpr int K_BLOCKS = BN * (KCH + 1) / 64;  // 1 KB LDS-load blocks per K tile (pad chunks included)
+  static constexpr int V_BLOCKS = BN * VCH / 64;
+  static constexpr int K_PER_WAVE = (K_BLOCKS + kWaves - 1) / kWaves;
+  static constexpr int V_PER_WAVE = V_BLOCKS / kWaves;
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
+  static constexpr int LDS_BYTES = 2 * V_TILE + 2 * K_TILE;
   // log2-domain growth of the running max tolerated before rescaling, and the
   // power-of-two shift applied to FP8 probabilities (p <= 2^(THRESH+SHIFT) <= 256)
   static constexpr float THRESH = FP8 ? 2.0f : 8.0f;
   static constexpr float SHIFT = FP8 ? 6.0f : 0.0f;
-  static_assert((BN / 4) * VCH == kHalf, "one V unit (4 keys x 16 bytes) per V-staging thread");
-  static_assert(K_TPR * BN == kHalf && K_LOADS * K_TPR == KCH, "K tile splits evenly over the K-staging threads");
+  static_assert((BN * (KCH + 1)) % 64 == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks");
+  static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
 };
 
 // Map the linear workgroup id to (batch*head, query tile).  Workgroups are
@@ -95,131 +107,101 @@ __device__ __forceinline__ void decode_item(int bid, int nblocks, int nqt, int& 
   qt = nqt - 1 - (item % nqt);
 }
 
-// Position of key k of a tile in a row of the transposed V tile (in elements).
-// BF16: P.V consumes 16 keys per MFMA; lane half hl holds keys 8a + 4hl + j of
-// each chunk in k-slot 4a + j, so the key's bits 2 and 3 swap.
-// FP8: P.V consumes 64 keys per MFMA; lane half hl holds keys 32bb + 8i + 4hl + j
-// in k-slot 16bb + 4i + j, stored at offset 32hl of the chunk.
+// XOR applied to the 16-byte chunk index of V row `key` in LDS.  It spreads the
+// rows that one transposing read touches over distinct banks: FP8 reads 8 keys
+// {0-3, 8-11} + base per lane group (key bits 1 and 3 vary), BF16 reads 4
+// consecutive keys (bits 0 and 1 vary).
 template <bool FP8>
-__device__ __forceinline__ int vt_pos(int k) {
+__device__ __forceinline__ int v_swizzle(int key) {
   if constexpr (FP8)
-    return (k & ~63) | (((k >> 2) & 1) << 5) | (((k >> 5) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+    return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2);
   else
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+    return (key & 3) << 2;
 }
 
-template <class C>
-struct TileRegs {
-  i32x4 r[C::NREG];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, I1).
+template <int I0, int I1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
+
+// Buffer load of 16 bytes per lane written straight to LDS: lane i's bytes land
+// at lds_block + 16 i (lds_block is wave-uniform).  Offsets at or beyond the
+// buffer size load zeros.
+//
+// Issued as inline assembly: the compiler then does not track these loads, so
+// it does not make the LDS reads of the current tile wait for the loads of the
+// next one (it cannot prove they touch different buffers).  The explicit
+// "s_waitcnt vmcnt(0)" before the barrier that ends the next phase is what
+// orders them.  M0 holds the LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, const uint8_t* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// Buffer resource words for raw 16-byte loads over [base, base + bytes): 32-bit
+// offsets, out-of-range offsets read zeros.  Wave-uniform.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// Workgroup barrier that also orders every memory access around it in the
+// compiler; with wait_loads the wave first waits for its own outstanding
+// global/buffer loads (including the LDS-writing ones).
+__device__ __forceinline__ void barrier(bool wait_loads) {
+  if (wait_loads)
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float lane_xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+__device__ __forceinline__ float lane_xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS reads (gfx950).  Within each group of 16 lanes, tr8: lane i
+// byte j = byte (i % 8) of the 8 bytes addressed by lane 2j + i/8; tr16: lane i
+// element j = element (i % 4) of the 4 halves addressed by lane 4j + i/4.
+__device__ __forceinline__ i32x2v lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)p);
+}
+__device__ __forceinline__ i16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+template <bool FP8>
+struct QOp;
+template <>
+struct QOp<true> {
+  using T = i32x8;
+};
+template <>
+struct QOp<false> {
+  using T = bf16x8;
 };
 
-// V-staging thread t (0..255) -> (4-key group kg, 16-byte channel chunk dc).  A
-// wave covers all key groups of two (FP8) or four (BF16) channel chunks.
-template <bool FP8>
-__device__ __forceinline__ void v_unit(int t, int& kg, int& dc) {
-  if constexpr (FP8) {
-    kg = t & 31;
-    dc = t >> 5;
-  } else {
-    kg = t & 15;
-    dc = t >> 4;
-  }
-}
-
-// Global -> registers.  Threads 0..255 fetch the V tile (4 keys x 16 bytes
-// each), threads 256..511 the K tile.  Rows at or beyond N read as zeros
-// (buffer bounds), so a ragged last tile needs no branches; keys >= N lie
-// above the diagonal of every valid query and are masked later.
-template <class C, bool FP8>
-__device__ __forceinline__ void load_tile(TileRegs<C>& t, const uint8_t* K, const uint8_t* V, uint32_t k_pitch,
-                                          uint32_t v_pitch, int kb, int N, int tid) {
-  const uint32_t rows = (uint32_t)min(N - kb, C::BN);
-  if (__builtin_amdgcn_readfirstlane(tid) < kHalf) {  // wave-uniform role
-    const auto rv = make_rsrc(V + (size_t)kb * v_pitch, rows * v_pitch);
-    int kg, dc;
-    v_unit<FP8>(tid, kg, dc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.r[i] = bload16(rv, (uint32_t)(4 * kg + i) * v_pitch + dc * 16);
-  } else {
-    const auto rk = make_rsrc(K + (size_t)kb * k_pitch, rows * k_pitch);
-    const int tk = tid - kHalf, r = tk / C::K_TPR, ch0 = (tk % C::K_TPR) * C::K_LOADS;
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) t.r[i] = bload16(rk, (uint32_t)r * k_pitch + (ch0 + i) * 16);
-  }
-}
-
-// Registers -> LDS stage: K rows as they are (padded pitch), V transposed to
-// channel rows with the key order of vt_pos.
-template <class C, bool FP8>
-__device__ __forceinline__ void store_tile(const TileRegs<C>& t, uint8_t* Ks, uint8_t* Vt, int tid) {
-  if (__builtin_amdgcn_readfirstlane(tid) >= kHalf) {  // wave-uniform role
-    const int tk = tid - kHalf, r = tk / C::K_TPR, ch0 = (tk % C::K_TPR) * C::K_LOADS;
-    uint8_t* dst = Ks + r * C::K_STRIDE + ch0 * 16;
-#pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) lds_store16(dst + i * 16, t.r[i]);
-    return;
-  }
-  int kg, dc;
-  v_unit<FP8>(tid, kg, dc);
-  const int pos = vt_pos<FP8>(4 * kg) * C::EB;
-  if constexpr (FP8) {
-    // dword e of each 16-byte chunk holds channels 4e..4e+3 of one key; write
-    // channel rows 16dc + 4e + {0..3}, 4 keys (4 bytes) each.
-    uint8_t* dst = Vt + dc * 16 * C::VT_STRIDE + pos;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t x0 = (uint32_t)t.r[0][e], x1 = (uint32_t)t.r[1][e];
-      const uint32_t x2 = (uint32_t)t.r[2][e], x3 = (uint32_t)t.r[3][e];
-      const uint32_t t01l = perm(x1, x0, 0x05010400u), t01h = perm(x1, x0, 0x07030602u);
-      const uint32_t t23l = perm(x3, x2, 0x05010400u), t23h = perm(x3, x2, 0x07030602u);
-      uint8_t* row = dst + 4 * e * C::VT_STRIDE;
-      lds_store4(row, (int)perm(t23l, t01l, 0x05040100u));
-      lds_store4(row + C::VT_STRIDE, (int)perm(t23l, t01l, 0x07060302u));
-      lds_store4(row + 2 * C::VT_STRIDE, (int)perm(t23h, t01h, 0x05040100u));
-      lds_store4(row + 3 * C::VT_STRIDE, (int)perm(t23h, t01h, 0x07060302u));
-    }
-  } else {
-    // dword e holds channels 2e, 2e+1 of one key; write channel rows
-    // 8dc + 2e + {0, 1}, 4 keys (8 bytes) each.
-    uint8_t* dst = Vt + dc * 8 * C::VT_STRIDE + pos;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t x0 = (uint32_t)t.r[0][e], x1 = (uint32_t)t.r[1][e];
-      const uint32_t x2 = (uint32_t)t.r[2][e], x3 = (uint32_t)t.r[3][e];
-      uint8_t* row = dst + 2 * e * C::VT_STRIDE;
-      lds_store8(row, i32x2{(int)perm(x1, x0, 0x05040100u), (int)perm(x3, x2, 0x05040100u)});
-      lds_store8(row + C::VT_STRIDE, i32x2{(int)perm(x1, x0, 0x07060302u), (int)perm(x3, x2, 0x07060302u)});
-    }
-  }
-}
-
-template <bool FP8>
-using QOperand = typename std::conditional<FP8, i32x8, bf16x8>::type;
-
-// S^T (32 keys x 32 queries per block) = K_tile * Q^T for the first nb blocks.
-template <class C, bool FP8>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::NBLK], const uint8_t* Ks,
-                                        const QOperand<FP8> (&q)[C::QK_STEPS], int l32, int hl) {
-#pragma unroll
-  for (int blk = 0; blk < C::NBLK; ++blk) {
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int kk = 0; kk < C::QK_STEPS; ++kk) {
-      if constexpr (FP8) {
-        const uint8_t* src = Ks + (blk * 32 + l32) * C::K_STRIDE + kk * 64 + hl * 32;
-        const i32x4 lo = lds_load16(src), hi = lds_load16(src + 16);
-        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc = mfma_fp8_32x32x64(a, q[kk], acc);
-      } else {
-        const i32x4 a = lds_load16(Ks + (blk * 32 + l32) * C::K_STRIDE + kk * 32 + hl * 16);
-        acc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), q[kk], acc);
-      }
-    }
-    s[blk] = acc;
-  }
-}
-
-// Running state of one wave's 32 queries.
 template <int DV>
 struct RowState {
   f32x16 o[DV / 32];  // O^T accumulator: lane owns query l % 32, channels 32d + 8i + 4hl + j
@@ -228,113 +210,53 @@ struct RowState {
   f32x4 l4;           // FP8: the full row sum (every entry)
 };
 
-// Online softmax of one tile and the P.V product.  MASK: the tile crosses the
-// diagonal (keys above a query are set to -inf first).
-template <class C, bool FP8, bool MASK, int DV>
-__device__ __forceinline__ void softmax_pv(f32x16 (&s)[C::NBLK], RowState<DV>& st, const uint8_t* Vt, float c,
-                                           int key_minus_query, int l32, int hl, const i32x8& sel) {
-  constexpr int NBLK = C::NBLK;
-  if constexpr (MASK) {
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (key_minus_query + blk * 32 + 8 * (r >> 2) + (r & 3) > 0) s[blk][r] = -INFINITY;
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[blk][r], s[blk][r + 1]));
-  mx = fmaxf(mx, xor32(mx));
-  const float mt = mx * c;
-  if (__any(mt > st.m + C::THRESH)) {  // wave-uniform; rare once the max settles
-    const float m_new = fmaxf(st.m, mt);
-    const float alpha = fast_exp2(st.m - m_new);
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d) st.o[d] *= alpha;
-    st.l *= alpha;
-    st.l4 *= alpha;
-    st.m = m_new;
-  }
-  const float bias = C::SHIFT - st.m;
+template <class C, bool FP8, int DQK, int DV>
+struct Wave {
+  static constexpr int NBLK = C::NBLK;
+  // per-lane LDS byte offsets (relative to a buffer)
+  int k_lane;               // K operand: row l % 32, k-half
+  int v_lane[DV / 32];      // V^T operand per 32-channel block
+  uint32_t k_dma[C::K_PER_WAVE];
+  uint32_t v_dma[C::V_PER_WAVE];
+  typename QOp<FP8>::T q[C::QK_STEPS];
+  f32x16 s[NBLK];
+  uint32_t pk[FP8 ? C::BN / 8 : C::BN / 4];  // this lane's probabilities of the tile (half its keys), MFMA B-operand order
+  RowState<DV> st;
+};
 
-  if constexpr (FP8) {
-#pragma unroll
-    for (int ks = 0; ks < C::BN / 64; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t pk[8];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) e[jj] = fast_exp2(__builtin_fmaf(s[2 * ks + hb][4 * i + jj], c, bias));
-          pk[4 * hb + i] = pack_fp8x4(e[0], e[1], e[2], e[3]);
-        }
-      const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
-                        (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
-      st.l4 = mfma_fp8_16x16x128(sel, pb, st.l4);
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d) {
-        const uint8_t* src = Vt + (d * 32 + l32) * C::VT_STRIDE + ks * 64 + hl * 32;
-        const i32x4 lo = lds_load16(src), hi = lds_load16(src + 16);
-        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        st.o[d] = mfma_fp8_32x32x64(a, pb, st.o[d]);
-      }
-    }
-  } else {
-    const uint32_t ones = 0x3f803f80u;  // two bf16 1.0
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        __builtin_amdgcn_sched_barrier(0);
-        uint32_t pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 8 * half + 2 * i;
-          const float p0 = fast_exp2(__builtin_fmaf(s[blk][r], c, bias));
-          const float p1 = fast_exp2(__builtin_fmaf(s[blk][r + 1], c, bias));
-          pk[i] = pack_bf16x2(p0, p1);
-          st.l = dot2_bf16(pk[i], ones, st.l);
-        }
-        const i32x4 pw = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const int chunk = 2 * blk + half;
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) {
-          const i32x4 a = lds_load16(Vt + (d * 32 + l32) * C::VT_STRIDE + chunk * 32 + hl * 16);
-          st.o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), pb, st.o[d]);
-        }
-      }
-  }
-}
+}  // namespace
 
 template <int DQK, int DV, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
   constexpr int NBLK = C::NBLK;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * C::STAGE_BYTES];
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  uint8_t* const Vs = smem;                 // V buffers 0, 1
+  uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
+  const int grp = w >> 2;  // 0: matrix work on even phases, 1: on odd phases
   const int N = p.N;
   const int nqt = (N + kBM - 1) / kBM;
   int bh, qt;
   decode_item(blockIdx.x, gridDim.x, nqt, bh, qt);
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / (p.Hq / p.Hkv);
   const int q0 = qt * kBM;
-  const int qw0 = q0 + 32 * w;  // first query of this wave
-  const int my_q = qw0 + l32;   // query owned by this lane
+  // SIMD s runs waves s (group 0) and s + 4 (group 1); they own query blocks
+  // 2s and 2s + 1, so both groups have work on the diagonal tiles.
+  const int qblk = 2 * (w & 3) + grp;
+  const int qw0 = q0 + 32 * qblk;  // first query of this wave
+  const int my_q = qw0 + l32;      // query owned by this lane
 
-  const size_t q_pitch = (size_t)p.Hq * C::KROW;  // bytes between consecutive positions
-  const uint32_t k_pitch = (uint32_t)p.Hkv * C::KROW;  // the host bounds Hkv * d * bytes per element
-  const uint32_t v_pitch = (uint32_t)p.Hkv * DV * C::EB;
+  const uint32_t q_pitch = (uint32_t)p.Hq * C::KROW;  // bytes between consecutive positions
+  const uint32_t k_pitch = (uint32_t)p.Hkv * C::KROW;
+  const uint32_t v_pitch = (uint32_t)p.Hkv * C::VROW;
   const uint8_t* Q = static_cast<const uint8_t*>(p.q) + ((size_t)b * N * p.Hq + h) * C::KROW;
   const uint8_t* K = static_cast<const uint8_t*>(p.k) + ((size_t)b * N * p.Hkv + g) * C::KROW;
-  const uint8_t* V = static_cast<const uint8_t*>(p.v) + ((size_t)b * N * p.Hkv + g) * DV * C::EB;
+  const uint8_t* V = static_cast<const uint8_t*>(p.v) + ((size_t)b * N * p.Hkv + g) * C::VROW;
 
   float c = p.sm_scale_log2;  // log2-domain score scale (dequantisation folded in for FP8)
   float sv = 1.f;
@@ -343,75 +265,304 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
     sv = p.v_scale[b * p.Hkv + g];
   }
 
-  // Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16), lane
-  // half hl holds 8 of them; FP8: k-step kk = channels [64kk, 64kk+64), 32 each.
-  QOperand<FP8> qreg[C::QK_STEPS];
+  Wave<C, FP8, DQK, DV> wv;
+
+  // ---- per-lane LDS offsets of the operand reads
+  wv.k_lane = l32 * C::KPITCH + hl * (FP8 ? 32 : 16);
+  {
+    const int grp16 = lane >> 4, s16 = lane & 15;
+    const int lhl = grp16 >> 1, gc = grp16 & 1;
 #pragma unroll
-  for (int kk = 0; kk < C::QK_STEPS; ++kk) {
-    if constexpr (FP8) {
-      const uint8_t* src = Q + (size_t)my_q * q_pitch + kk * 64 + hl * 32;
-      const i32x4 lo = gload16(src, my_q < N), hi = gload16(src + 16, my_q < N);
-      qreg[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      qreg[kk] = __builtin_bit_cast(bf16x8, gload16(Q + (size_t)my_q * q_pitch + kk * 32 + hl * 16, my_q < N));
+    for (int db = 0; db < DV / 32; ++db) {
+      if constexpr (FP8) {
+        // source lane s16 = 2j + hh reads 8 bytes: key 8(j/4) + 4hl + j%4,
+        // channels 32db + 16gc + 8hh .. +8
+        const int j = s16 >> 1, hh = s16 & 1;
+        const int key = 8 * (j >> 2) + 4 * lhl + (j & 3);
+        const int ch = 2 * db + gc;
+        wv.v_lane[db] = key * C::VROW + 16 * (ch ^ v_swizzle<true>(key)) + 8 * hh;
+      } else {
+        // source lane s16 = 4j + qq reads 4 halves: key 4hl + j, channels
+        // 32db + 16gc + 4qq .. +4
+        const int j = s16 >> 2, qq = s16 & 3;
+        const int key = 4 * lhl + j;
+        const int ch = 4 * db + 2 * gc + (qq >> 1);
+        wv.v_lane[db] = key * C::VROW + 16 * (ch ^ v_swizzle<false>(key)) + 8 * (qq & 1);
+      }
     }
+  }
+  // ---- per-lane global offsets of the tile loads (tile-relative, the same for every tile)
+#pragma unroll
+  for (int i = 0; i < C::K_PER_WAVE; ++i) {
+    const int blk = w + kWaves * i;
+    const int pos = 64 * blk + lane, row = pos / (C::KCH + 1), ch = pos % (C::KCH + 1);
+    wv.k_dma[i] = (ch < C::KCH) ? (uint32_t)row * k_pitch + 16u * ch : 0x80000000u;  // pad chunks load zeros
+  }
+#pragma unroll
+  for (int i = 0; i < C::V_PER_WAVE; ++i) {
+    const int blk = w + kWaves * i;
+    const int pos = 64 * blk + lane, key = pos / C::VCH, slot = pos % C::VCH;
+    wv.v_dma[i] = (uint32_t)key * v_pitch + 16u * (slot ^ v_swizzle<FP8>(key));
   }
 
   const int kend = min(q0 + kBM, N);
-  const int ntiles = (kend + C::BN - 1) / C::BN;
-  const int first_diag = q0 / C::BN;  // tiles from here on may hold keys above the diagonal
+  const int T = (kend + BN - 1) / BN;  // key tiles of the workgroup
+  // tiles this wave needs: keys up to its last valid query
+  const int Tw = qw0 < N ? (min(qw0 + 31, N - 1) / BN + 1) : 0;
 
-  // Prologue: tile 0 into LDS stage 0, tile 1 in flight in registers.
-  TileRegs<C> pre;
-  load_tile<C, FP8>(pre, K, V, k_pitch, v_pitch, 0, N, tid);
-  store_tile<C, FP8>(pre, smem, smem + C::K_BYTES, tid);
-  if (ntiles > 1) load_tile<C, FP8>(pre, K, V, k_pitch, v_pitch, C::BN, N, tid);
-
-  RowState<DV> st;
+  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const int kb = t * BN;
+    const i32x4 rk = rsrc_words(K + (size_t)kb * k_pitch, (uint32_t)min(N - kb, BN) * k_pitch);
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d) st.o[d] = zero16();
-  st.m = -1e30f;
-  st.l = 0.f;
-  st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < C::K_PER_WAVE; ++i) {
+      const int blk = w + kWaves * i;
+      if (blk < C::K_BLOCKS) load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
+    }
+  };
+  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const int kb = t * BN;
+    const i32x4 rv = rsrc_words(V + (size_t)kb * v_pitch, (uint32_t)min(N - kb, BN) * v_pitch);
+#pragma unroll
+    for (int i = 0; i < C::V_PER_WAVE; ++i) {
+      const int blk = w + kWaves * i;
+      load_to_lds(rv, wv.v_dma[i], Vs + buf * C::V_TILE + 1024 * blk);
+    }
+  };
+  // loads of step p: K tile p+1 and V tile p
+  auto issue_step = [&](int pstep) __attribute__((always_inline)) {
+    if (pstep + 1 < T) issue_k(pstep + 1, (pstep + 1) & 1);
+    if (pstep < T) issue_v(pstep, pstep & 1);
+  };
+
+  // ---- Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16),
+  // lane half hl holds 8 of them; FP8: k-step kk = channels [64kk, 64kk+64), 32 each.
+  {
+    const uint32_t rows = (uint32_t)max(0, min(32, N - qw0));
+    const auto rq = make_rsrc(Q + (size_t)min(qw0, N) * q_pitch, rows * q_pitch);
+#pragma unroll
+    for (int kk = 0; kk < C::QK_STEPS; ++kk) {
+      if constexpr (FP8) {
+        const uint32_t off = (uint32_t)l32 * q_pitch + kk * 64 + hl * 32;
+        const i32x4 lo = bload16(rq, off), hi = bload16(rq, off + 16);
+        wv.q[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        wv.q[kk] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)l32 * q_pitch + kk * 32 + hl * 16));
+      }
+    }
+    // Pass the Q registers through an empty asm so the compiler waits for these
+    // loads here, once, instead of at their first use inside the loop (where
+    // the wait would also stall on the tile loads in flight).
+#pragma unroll
+    for (int kk = 0; kk < C::QK_STEPS; ++kk) asm volatile("" : "+v"(wv.q[kk]));
+  }
+
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d) wv.st.o[d] = zero16();
+  wv.st.m = -1e30f;
+  wv.st.l = 0.f;
+  wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
   // FP8 row-sum selector: 16x16x128 A operand, 1.0 where the lane group's
   // parity matches its row group's parity, else 0.
   const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
   const i32x8 sel = {sel_on, sel_on, sel_on, sel_on, sel_on, sel_on, sel_on, sel_on};
 
-  // One tile; the LDS stage is a compile-time constant so every LDS access is a
-  // per-lane base plus an immediate offset.
-  auto tile_step = [&](int j, auto stage_tag) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_tag)::value;
-    uint8_t* const cur_k = smem + S * C::STAGE_BYTES;
-    uint8_t* const cur_v = cur_k + C::K_BYTES;
-    uint8_t* const nxt_k = smem + (1 - S) * C::STAGE_BYTES;
-    uint8_t* const nxt_v = nxt_k + C::K_BYTES;
-    __syncthreads();  // tile j is visible; every wave is done with tile j-1
-    if (j + 1 < ntiles) store_tile<C, FP8>(pre, nxt_k, nxt_v, tid);
-    if (j + 2 < ntiles) load_tile<C, FP8>(pre, K, V, k_pitch, v_pitch, (j + 2) * C::BN, N, tid);
-
-    const int kb = j * C::BN;
-    if (kb > qw0 + 31) return;  // the whole tile lies above this wave's queries
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s[NBLK];
-    qk_tile<C, FP8>(s, cur_k, qreg, l32, hl);
-    __builtin_amdgcn_sched_barrier(0);
-    if (j < first_diag)
-      softmax_pv<C, FP8, false, DV>(s, st, cur_v, c, 0, l32, hl, sel);
-    else
-      softmax_pv<C, FP8, true, DV>(s, st, cur_v, c, kb + 4 * hl - my_q, l32, hl, sel);
+  // ---- matrix work of step pstep: P_{pstep-1} V_{pstep-1}, then S_pstep = K_pstep Q^T.
+  // The products form one list of MFMAs (PV first, then QK with the k-steps
+  // outermost so consecutive MFMAs are independent); the LDS operand of MFMA
+  // i+1 is read while MFMA i runs.
+  constexpr int PV_OPS = FP8 ? (BN / 64) * (DV / 32) : (BN / 16) * (DV / 32);
+  constexpr int QK_OPS = NBLK * C::QK_STEPS;
+  using AOp = typename std::conditional<FP8, i32x8, i32x4>::type;
+  auto fetch = [&](int i, const uint8_t* vb, const uint8_t* kb) __attribute__((always_inline)) -> AOp {
+    AOp a;
+    if (i < PV_OPS) {
+      if constexpr (FP8) {
+        const int ks = i / (DV / 32), db = i % (DV / 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const i32x2v t = lds_tr8(vb + wv.v_lane[db] + (64 * ks + 32 * (r >> 1) + 16 * (r & 1)) * C::VROW);
+          a[2 * r] = t[0];
+          a[2 * r + 1] = t[1];
+        }
+      } else {
+        const int chunk = i / (DV / 32), db = i % (DV / 32);
+        const i16x4 t0 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk) * C::VROW);
+        const i16x4 t1 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk + 8) * C::VROW);
+        const i32x2v u0 = __builtin_bit_cast(i32x2v, t0), u1 = __builtin_bit_cast(i32x2v, t1);
+        a = i32x4{u0[0], u0[1], u1[0], u1[1]};
+      }
+    } else {
+      const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
+      if constexpr (FP8) {
+        const uint8_t* src = kb + blk * 32 * C::KPITCH + kk * 64;
+        const i32x4 lo = lds_load16(src), hi = lds_load16(src + 16);
+        a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        a = lds_load16(kb + blk * 32 * C::KPITCH + kk * 32);
+      }
+    }
+    return a;
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile_step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntiles) tile_step(j + 1, std::integral_constant<int, 1>{});
+  auto mma = [&](int i, const AOp& a) __attribute__((always_inline)) {
+    if (i < PV_OPS) {
+      if constexpr (FP8) {
+        const int ks = i / (DV / 32), db = i % (DV / 32);
+        const i32x8 pb = {(int)wv.pk[8 * ks + 0], (int)wv.pk[8 * ks + 1], (int)wv.pk[8 * ks + 2],
+                          (int)wv.pk[8 * ks + 3], (int)wv.pk[8 * ks + 4], (int)wv.pk[8 * ks + 5],
+                          (int)wv.pk[8 * ks + 6], (int)wv.pk[8 * ks + 7]};
+        if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
+        wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
+      } else {
+        const int chunk = i / (DV / 32), db = i % (DV / 32);
+        const i32x4 pw = {(int)wv.pk[4 * chunk], (int)wv.pk[4 * chunk + 1], (int)wv.pk[4 * chunk + 2],
+                          (int)wv.pk[4 * chunk + 3]};
+        wv.st.o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pw), wv.st.o[db]);
+      }
+    } else {
+      const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
+      const f32x16 acc = kk == 0 ? zero16() : wv.s[blk];
+      if constexpr (FP8)
+        wv.s[blk] = mfma_fp8_32x32x64(a, wv.q[kk], acc);
+      else
+        wv.s[blk] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), wv.q[kk], acc);
+    }
+  };
+  // LDS reads of the operand of list entry i, and MFMAs it issues
+  auto n_reads = [](int i) constexpr { return i < PV_OPS ? (FP8 ? 4 : 2) : (FP8 ? 2 : 1); };
+  auto n_mfma = [](int i) constexpr { return (FP8 && i < PV_OPS && i % (DV / 32) == 0) ? 2 : 1; };
+  // MFMAs [i0, i1) of the list; the operand of MFMA i+2 is read before MFMA i
+  // issues (three operand buffers), an order pinned with scheduling groups.
+  auto run_ops = [&](auto i0_tag, auto i1_tag, const uint8_t* vb, const uint8_t* kb) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
+    AOp buf[3];
+    buf[0] = fetch(I0, vb, kb);
+    __builtin_amdgcn_sched_group_barrier(0x100, n_reads(I0), 0);
+    if constexpr (I0 + 1 < I1) {
+      buf[1] = fetch(I0 + 1, vb, kb);
+      __builtin_amdgcn_sched_group_barrier(0x100, n_reads(I0 + 1), 0);
+    }
+    static_for<I0, I1>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 2 < I1) {
+        buf[(i + 2 - I0) % 3] = fetch(i + 2, vb, kb);
+        __builtin_amdgcn_sched_group_barrier(0x100, n_reads(i + 2), 0);
+      }
+      mma(i, buf[(i - I0) % 3]);
+      __builtin_amdgcn_sched_group_barrier(0x008, n_mfma(i), 0);
+    });
+  };
+  auto matrix_work = [&](int pstep, auto parity) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(parity)::value;  // pstep & 1
+    const uint8_t* vb = Vs + (1 - PAR) * C::V_TILE;       // V tile pstep-1
+    const uint8_t* kb = Ks + PAR * C::K_TILE + wv.k_lane;  // K tile pstep
+    // One instruction sequence for every step the wave takes part in (a single
+    // variant keeps the register allocation tight): at step 0 the P.V product
+    // multiplies zero probabilities with a zero-filled V buffer, and at step Tw
+    // the scores of a tile the wave does not need are computed and never read.
+    if (pstep <= Tw)
+      run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
+  };
+
+  // ---- vector work of step pstep: online softmax of S_pstep -> probabilities.
+  auto vector_work = [&](int pstep) __attribute__((always_inline)) {
+    if (pstep < 0 || pstep >= Tw) return;
+    const int kb = pstep * BN;
+    if (kb + BN - 1 > qw0) {  // the tile crosses this wave's diagonal: mask keys above each query
+      // key offset k of register r is visible iff k <= lim; the sign of lim - k
+      // selects -inf bit by bit (no per-element compare masks held in SGPRs)
+      const int lim = my_q - kb - 4 * hl;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t hide = (uint32_t)((lim - (blk * 32 + 8 * (r >> 2) + (r & 3))) >> 31);
+          const float x = wv.s[blk][r];  // scalar copy before the bit cast
+          wv.s[blk][r] = __uint_as_float((hide & 0xff800000u) | (~hide & __float_as_uint(x)));
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(wv.s[blk][r], wv.s[blk][r + 1]));
+    mx = lane_xor32_max(mx);
+    const float mt = mx * c;
+    if (__any(mt > wv.st.m + C::THRESH)) {  // wave-uniform; rare once the max settles
+      const float m_new = fmaxf(wv.st.m, mt);
+      const float alpha = fast_exp2(wv.st.m - m_new);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) wv.st.o[d] *= alpha;
+      wv.st.l *= alpha;
+      wv.st.l4 *= alpha;
+      wv.st.m = m_new;
+    }
+    const float bias = C::SHIFT - wv.st.m;
+    if constexpr (FP8) {
+      // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) e[jj] = fast_exp2(__builtin_fmaf(wv.s[blk][4 * i + jj], c, bias));
+          wv.pk[4 * blk + i] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+        }
+    } else {
+      const uint32_t ones = 0x3f803f80u;  // two bf16 1.0
+      // pk[2r' + e] with r' = 8blk + ... : register pair (r, r+1) of block blk
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(wv.s[blk][2 * i], c, bias));
+          const float p1 = fast_exp2(__builtin_fmaf(wv.s[blk][2 * i + 1], c, bias));
+          const uint32_t pp = pack_bf16x2(p0, p1);
+          wv.pk[8 * blk + i] = pp;
+          wv.st.l = dot2_bf16(pp, ones, wv.st.l);
+        }
+    }
+  };
+
+  // ---- prologue: K tile 0 into buffer 0; V buffer 1 (read by the empty P.V
+  // product of step 0) and the probabilities start at zero.
+  issue_k(0, 0);
+#pragma unroll
+  for (int i = 0; i < C::V_TILE / (16 * kThreads); ++i)
+    lds_store16(Vs + C::V_TILE + 16 * (tid + kThreads * i), i32x4{0, 0, 0, 0});
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(wv.pk) / sizeof(wv.pk[0])); ++i) wv.pk[i] = 0u;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (grp == 1) {
+    issue_step(0);
+    barrier(false);  // group B starts one phase later
   }
 
-  // Epilogue: normalise by the row sum and store BF16.
+  // ---- main loop: steps 0..T (step T only drains P_{T-1} V_{T-1})
+  // Both groups run the same matrix/vector code; only where each issues its
+  // share of the tile loads and which barrier waits for them differ:
+  //   group A: loads(p), matrix(p) | barrier | vector(p), wait | barrier
+  //   group B: matrix(p), wait | barrier | loads(p+1), vector(p) | barrier
+  auto step = [&](int ps, auto parity) __attribute__((always_inline)) {
+    if (grp == 0) issue_step(ps);
+    matrix_work(ps, parity);
+    barrier(grp != 0);
+    if (grp != 0) issue_step(ps + 1);
+    vector_work(ps);
+    barrier(grp == 0);
+  };
+  for (int ps = 0; ps <= T; ps += 2) {
+    step(ps, std::integral_constant<int, 0>{});
+    if (ps + 1 <= T) step(ps + 1, std::integral_constant<int, 1>{});
+  }
+  if (grp == 0) barrier(false);
+
+  // ---- epilogue: normalise by the row sum and store BF16
   float inv;
   if constexpr (FP8) {
-    inv = sv / st.l4[0];
+    inv = sv / wv.st.l4[0];
   } else {
-    inv = 1.0f / (st.l + xor32(st.l));
+    inv = 1.0f / lane_xor32_sum(wv.st.l);
   }
   if (my_q < N) {
     __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * N + my_q) * p.Hq + h) * DV;
@@ -420,15 +571,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ch = d * 32 + 8 * i + 4 * hl;
-        const i32x2 v2 = {(int)pack_bf16x2(st.o[d][4 * i] * inv, st.o[d][4 * i + 1] * inv),
-                          (int)pack_bf16x2(st.o[d][4 * i + 2] * inv, st.o[d][4 * i + 3] * inv)};
+        const i32x2 v2 = {(int)pack_bf16x2(wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv),
+                          (int)pack_bf16x2(wv.st.o[d][4 * i + 2] * inv, wv.st.o[d][4 * i + 3] * inv)};
         *reinterpret_cast<i32x2*>(O + ch) = v2;
       }
     }
   }
 }
-
-}  // namespace
 
 int attn_fwd_workgroups(int B, int Hq, int N) {
   const long long nqt = (N + kBM - 1) / kBM;
