@@ -186,6 +186,9 @@ def main(argv=None):
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="before the warmup, run one plain elementwise copy (torch.neg) that reads and writes "
+                         "this many bytes: the reference kernel of known traffic for scaling HBM counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path is a single-GPU kernel and this build has no "
@@ -200,6 +203,12 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     w = WORKLOADS[args.workload]
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     ms, attn_ms = run_gpu(w, args.steps, args.warmup)
     value = w.causal_flops / (ms * 1e-3) / 1e12
     rec = {

@@ -89,6 +89,9 @@ struct Cfg {
   // power-of-two shift applied to FP8 probabilities (p <= 2^(THRESH+SHIFT) <= 256)
   static constexpr float THRESH = FP8 ? 2.0f : 8.0f;
   static constexpr float SHIFT = FP8 ? 6.0f : 0.0f;
+  // FP8 probabilities are written as e4m3 codes straight from the log2-domain
+  // score ("lean P"): the code of 2^x is about 8x + 56, exact at integer x.
+  static constexpr bool LEAN_P = FP8;
   static_assert((BN * (KCH + 1)) % 64 == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks");
   static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
 };
@@ -208,7 +211,36 @@ struct RowState {
   float m;            // running max, log2 domain
   float l;            // BF16: this lane's share of the row sum
   f32x4 l4;           // FP8: the full row sum (every entry)
+  float kc;           // lean P: integer code offset K = 8 (SHIFT - m) + C0 (m kept on that grid)
 };
+
+// Lean P.  The e4m3 code of 2^x (x in [-6, 8]) is 8x + 56 at integer x and
+// linear in between, so a probability's code is round(8 x + C0) with x = s c -
+// m + SHIFT.  One FMA computes MAGIC + 8 s c + K (K = 8 (SHIFT - m) + C0, an
+// integer because m is kept on that grid): with MAGIC = 1.5 * 2^23 the float's
+// low mantissa byte is the rounded code.  One max against MAGIC clamps codes below 0
+// (the float then equals MAGIC: code 0, also for masked -inf scores) and writes
+// that low byte into the packed probability word (SDWA byte select).  C0 centres
+// the error of the linear mantissa: 55.66 minimises the largest log error over
+// an octave.
+constexpr float kLeanC0 = 55.66f;
+constexpr float kLeanMagic = 12582912.0f;  // 1.5 * 2^23
+
+// Codes of four scores into one word, first score in the low byte.
+__device__ __forceinline__ uint32_t lean_p4(float s0, float s1, float s2, float s3, float c8, float b8, float magic) {
+  const float t0 = __builtin_fmaf(s0, c8, b8), t1 = __builtin_fmaf(s1, c8, b8);
+  const float t2 = __builtin_fmaf(s2, c8, b8), t3 = __builtin_fmaf(s3, c8, b8);
+  uint32_t w;
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+      : "=v"(w) : "v"(t0), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t1), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t2), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t3), "v"(magic));
+  return w;
+}
 
 template <class C, bool FP8, int DQK, int DV>
 struct Wave {
@@ -361,6 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   wv.st.m = -1e30f;
   wv.st.l = 0.f;
   wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  wv.st.kc = 0.f;
   // FP8 row-sum selector: 16x16x128 A operand, 1.0 where the lane group's
   // parity matches its row group's parity, else 0.
   const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
@@ -480,15 +513,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
           wv.s[blk][r] = __uint_as_float((hide & 0xff800000u) | (~hide & __float_as_uint(x)));
         }
     }
-    float mx = -INFINITY;
+    // row max: four independent chains of 3-input max (two new values each)
+    float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(wv.s[blk][r], wv.s[blk][r + 1]));
+      for (int r = 0; r < 16; r += 2) {
+        float& m = mc[(blk * 8 + r / 2) & 3];
+        m = fmaxf(fmaxf(m, wv.s[blk][r]), wv.s[blk][r + 1]);
+      }
+    float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
     mx = lane_xor32_max(mx);
     const float mt = mx * c;
     if (__any(mt > wv.st.m + C::THRESH)) {  // wave-uniform; rare once the max settles
-      const float m_new = fmaxf(wv.st.m, mt);
+      float m_new = fmaxf(wv.st.m, mt);
+      if constexpr (C::LEAN_P) {
+        // round the new max up onto the grid where K = 8 (SHIFT - m) + C0 is an integer
+        const float kc = floorf(8.f * (C::SHIFT - m_new) + kLeanC0);
+        const bool up = mt > wv.st.m;
+        m_new = up ? C::SHIFT + (kLeanC0 - kc) * 0.125f : wv.st.m;
+        wv.st.kc = up ? kc : wv.st.kc;
+      }
       const float alpha = fast_exp2(wv.st.m - m_new);
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d) wv.st.o[d] *= alpha;
@@ -497,7 +542,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       wv.st.m = m_new;
     }
     const float bias = C::SHIFT - wv.st.m;
-    if constexpr (FP8) {
+    if constexpr (C::LEAN_P) {
+      // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
+      const float c8 = 8.f * c, b8 = kLeanMagic + wv.st.kc, magic = kLeanMagic;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wv.pk[4 * blk + i] = lean_p4(wv.s[blk][4 * i], wv.s[blk][4 * i + 1], wv.s[blk][4 * i + 2],
+                                       wv.s[blk][4 * i + 3], c8, b8, magic);
+    } else if constexpr (FP8) {
       // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)

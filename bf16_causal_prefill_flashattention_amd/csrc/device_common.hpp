@@ -16,6 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -46,8 +47,6 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) 
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // a.x * b.x + a.y * b.y + c with bf16 products accumulated in fp32.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -103,19 +102,23 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Round two fp32 to bf16 (nearest-even) and pack them, first value low.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round two fp32 to bf16 (nearest-even) and pack them, first value low: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a);
-  __bf16 y = static_cast<__bf16>(b);
-  uint16_t xu = __builtin_bit_cast(uint16_t, x);
-  uint16_t yu = __builtin_bit_cast(uint16_t, y);
-  return static_cast<uint32_t>(xu) | (static_cast<uint32_t>(yu) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Round four fp32 to OCP e4m3 (hardware conversion, nearest-even) and pack
 // them, first value in the low byte.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion writes the low half only; start from an undefined
+  // register (the high half is overwritten next) instead of materialising 0
+  int w;
+  asm("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return static_cast<uint32_t>(w);
 }
