@@ -48,10 +48,12 @@
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
 // accumulator.  The row sum is taken from the rounded probabilities that feed
-// the P.V product ([P3] "ZYFA 如何工作？", rounded row sums): for FP8 with one
-// extra 16x16x128 MFMA per 64 keys against a 0/1 selector matrix, for BF16 with
-// bf16 dot products.  FP8 probabilities are scaled by a fixed power of two
-// before rounding to e4m3, which the row sum cancels.
+// the P.V product ([P3] "ZYFA 如何工作？", rounded row sums), with one extra
+// small MFMA per P.V k-step against a 0/1 selector matrix (16x16x128 for FP8,
+// 16x16x32 for BF16).  It runs on the matrix core with the other MFMAs of the
+// wave: the vector-side dot-product instructions share the matrix pipeline and
+// stall behind the other wave's MFMAs.  FP8 probabilities are scaled by a fixed
+// power of two before rounding to e4m3, which the row sum cancels.
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -175,12 +177,6 @@ __device__ __forceinline__ float lane_xor32_max(float v) {
   return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
-__device__ __forceinline__ float lane_xor32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const uint32_t a = r[0], b = r[1];
-  return __uint_as_float(a) + __uint_as_float(b);
-}
-
 typedef int i32x2v __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -209,8 +205,7 @@ template <int DV>
 struct RowState {
   f32x16 o[DV / 32];  // O^T accumulator: lane owns query l % 32, channels 32d + 8i + 4hl + j
   float m;            // running max, log2 domain
-  float l;            // BF16: this lane's share of the row sum
-  f32x4 l4;           // FP8: the full row sum (every entry)
+  f32x4 l4;           // the full row sum (every entry)
   float kc;           // lean P: integer code offset K = 8 (SHIFT - m) + C0 (m kept on that grid)
 };
 
@@ -391,13 +386,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) wv.st.o[d] = zero16();
   wv.st.m = -1e30f;
-  wv.st.l = 0.f;
   wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
   wv.st.kc = 0.f;
-  // FP8 row-sum selector: 16x16x128 A operand, 1.0 where the lane group's
-  // parity matches its row group's parity, else 0.
-  const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
-  const i32x8 sel = {sel_on, sel_on, sel_on, sel_on, sel_on, sel_on, sel_on, sel_on};
+  // Row-sum selector (A operand of the 16x16 row-sum MFMA): 1.0 where the lane
+  // group's parity matches its row group's parity, else 0.  Lane l then finds
+  // the sum over the k-step's keys for its own query l % 32 in every entry of
+  // its D registers.
+  const bool sel_on = ((lane >> 4) & 1) == (((lane & 15) >> 2) & 1);
+  const int sel_w = sel_on ? (FP8 ? 0x38383838 : 0x3f803f80) : 0;  // e4m3 / bf16 ones
+  const i32x8 sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
 
   // ---- matrix work of step pstep: P_{pstep-1} V_{pstep-1}, then S_pstep = K_pstep Q^T.
   // The products form one list of MFMAs (PV first, then QK with the k-steps
@@ -449,6 +446,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
         const int chunk = i / (DV / 32), db = i % (DV / 32);
         const i32x4 pw = {(int)wv.pk[4 * chunk], (int)wv.pk[4 * chunk + 1], (int)wv.pk[4 * chunk + 2],
                           (int)wv.pk[4 * chunk + 3]};
+        if (db == 0)
+          wv.st.l4 = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(sel, sel, 0, 1, 2, 3)),
+                                        __builtin_bit_cast(bf16x8, pw), wv.st.l4);
         wv.st.o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pw), wv.st.o[db]);
       }
     } else {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   };
   // LDS reads of the operand of list entry i, and MFMAs it issues
   auto n_reads = [](int i) constexpr { return i < PV_OPS ? (FP8 ? 4 : 2) : (FP8 ? 2 : 1); };
-  auto n_mfma = [](int i) constexpr { return (FP8 && i < PV_OPS && i % (DV / 32) == 0) ? 2 : 1; };
+  auto n_mfma = [](int i) constexpr { return (i < PV_OPS && i % (DV / 32) == 0) ? 2 : 1; };
   // MFMAs [i0, i1) of the list; the operand of MFMA i+2 is read before MFMA i
   // issues (three operand buffers), an order pinned with scheduling groups.
   auto run_ops = [&](auto i0_tag, auto i1_tag, const uint8_t* vb, const uint8_t* kb) __attribute__((always_inline)) {
@@ -537,7 +537,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       const float alpha = fast_exp2(wv.st.m - m_new);
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d) wv.st.o[d] *= alpha;
-      wv.st.l *= alpha;
       wv.st.l4 *= alpha;
       wv.st.m = m_new;
     }
@@ -563,7 +562,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
           wv.pk[4 * blk + i] = pack_fp8x4(e[0], e[1], e[2], e[3]);
         }
     } else {
-      const uint32_t ones = 0x3f803f80u;  // two bf16 1.0
       // pk[2r' + e] with r' = 8blk + ... : register pair (r, r+1) of block blk
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
@@ -573,7 +571,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
           const float p1 = fast_exp2(__builtin_fmaf(wv.s[blk][2 * i + 1], c, bias));
           const uint32_t pp = pack_bf16x2(p0, p1);
           wv.pk[8 * blk + i] = pp;
-          wv.st.l = dot2_bf16(pp, ones, wv.st.l);
         }
     }
   };
@@ -612,12 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   if (grp == 0) barrier(false);
 
   // ---- epilogue: normalise by the row sum and store BF16
-  float inv;
-  if constexpr (FP8) {
-    inv = sv / wv.st.l4[0];
-  } else {
-    inv = 1.0f / lane_xor32_sum(wv.st.l);
-  }
+  const float inv = sv / wv.st.l4[0];
   if (my_q < N) {
     __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * N + my_q) * p.Hq + h) * DV;
 #pragma unroll

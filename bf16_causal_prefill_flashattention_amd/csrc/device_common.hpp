@@ -48,9 +48,11 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// a.x * b.x + a.y * b.y + c with bf16 products accumulated in fp32.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies 8 k-slots of
+// A row / B column (l % 16); lane group l / 16 selects which quarter of the 32
+// k-slots.  D: lane l holds column (l % 16), rows 4*(l / 16) + j in register j.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
