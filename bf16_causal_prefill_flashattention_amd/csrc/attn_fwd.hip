@@ -59,6 +59,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace miattn {
@@ -97,20 +98,6 @@ struct Cfg {
   static_assert((BN * (KCH + 1)) % 64 == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks");
   static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
 };
-
-// Map the linear workgroup id to (batch*head, query tile).  Workgroups are
-// dispatched round-robin over the 8 XCDs (id % 8), each XCD with its own L2;
-// giving every XCD a contiguous range of work items keeps the query tiles that
-// run together on an XCD on the same key/value head, so the K/V tiles they
-// stream are shared in that XCD's L2.  Within a head the heaviest (latest)
-// query tiles come first, so the short diagonal tiles fill the tail.
-__device__ __forceinline__ void decode_item(int bid, int nblocks, int nqt, int& bh, int& qt) {
-  const int xcd = bid & 7, j = bid >> 3;
-  const int base = nblocks >> 3, rem = nblocks & 7;
-  const int item = xcd * base + min(xcd, rem) + j;
-  bh = item / nqt;
-  qt = nqt - 1 - (item % nqt);
-}
 
 // XOR applied to the 16-byte chunk index of V row `key` in LDS.  It spreads the
 // rows that one transposing read touches over distinct banks: FP8 reads 8 keys
@@ -253,12 +240,14 @@ struct Wave {
 
 }  // namespace
 
+// One work item: the kBM queries of query tile qt of (batch, head) bh, against
+// all keys up to the last of them.  Called by every thread of the workgroup;
+// leaves no load in flight and no wave reading LDS when it returns.
 template <int DQK, int DV, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
+__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, int bh, int qt) {
   using C = Cfg<FP8, DQK, DV>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   uint8_t* const Vs = smem;                 // V buffers 0, 1
   uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
 
@@ -267,9 +256,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int grp = w >> 2;  // 0: matrix work on even phases, 1: on odd phases
   const int N = p.N;
-  const int nqt = (N + kBM - 1) / kBM;
-  int bh, qt;
-  decode_item(blockIdx.x, gridDim.x, nqt, bh, qt);
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / (p.Hq / p.Hkv);
   const int q0 = qt * kBM;
   // SIMD s runs waves s (group 0) and s + 4 (group 1); they own query blocks
@@ -625,15 +611,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-int attn_fwd_workgroups(int B, int Hq, int N) {
+// Persistent workgroups (at most one per CU) walk a static list of work units.
+// A unit is a pair of query tiles of one (batch, head), the j-th from the end
+// and the j-th from the start of the causal triangle, so every unit costs about
+// the same and the workgroups finish together (separate per-tile workgroups
+// left CUs idle between workgroups and at the tail).  Workgroup w runs on XCD
+// w % 8 (round-robin dispatch); when the (batch, head) count splits evenly over
+// the 8 XCDs, XCD x takes the heads bh = x (mod 8) and its workgroups sweep one
+// head at a time, so the K/V tiles they stream are shared in that XCD's L2.
+template <int DQK, int DV, bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
+  using C = Cfg<FP8, DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  const int nqt = (p.N + kBM - 1) / kBM;
+  const int npair = (nqt + 1) / 2;  // units per (batch, head)
+  const int nbh = p.B * p.Hq;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const bool by_xcd = (nbh % 8 == 0) && (G % 8 == 0);
+  const int rank = by_xcd ? wg / 8 : wg, nrank = by_xcd ? G / 8 : G;
+  const int nunit = by_xcd ? (nbh / 8) * npair : nbh * npair;
+  // one call site (the item body is large): the two tiles of a unit are
+  // iterations half = 0 (the later, heavier tile) and half = 1
+  int u = rank, half = 0;
+  while (u < nunit) {
+    const int bh = by_xcd ? 8 * (u / npair) + wg % 8 : u / npair;
+    const int j = u % npair;
+    const int qt = half == 0 ? nqt - 1 - j : j;
+    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8>(p, smem, bh, qt);
+    u += half * nrank;
+    half ^= 1;
+  }
+}
+
+long long attn_fwd_units(int B, int Hq, int N) {
   const long long nqt = (N + kBM - 1) / kBM;
-  const long long n = (long long)B * Hq * nqt;
-  return n > 0x7fffffffLL ? -1 : (int)n;
+  return (long long)B * Hq * ((nqt + 1) / 2);
 }
 
 hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream) {
-  const int grid = attn_fwd_workgroups(p.B, p.Hq, p.N);
-  if (grid <= 0) return hipErrorInvalidValue;
+  const long long units = attn_fwd_units(p.B, p.Hq, p.N);
+  if (units <= 0 || units > 0x7fffffffLL) return hipErrorInvalidValue;
+  static int cu_count[64];  // per device, filled on first use
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cu_count[dev] = n > 0 ? n : 1;
+  }
+  const int grid = (int)std::min<long long>(units, cu_count[dev]);
   const dim3 g(grid), blk(kThreads);
   if (d_v != 128) return hipErrorInvalidValue;
   if (dtype == 0) {

@@ -18,8 +18,9 @@ struct AttnParams {
   float sm_scale_log2;  // softmax scale times log2(e)
 };
 
-// Number of workgroups of one attention launch; -1 if it overflows int.
-int attn_fwd_workgroups(int B, int Hq, int N);
+// Work units of one attention launch (pairs of query tiles of one batch and
+// head); the launch runs min(units, CUs) persistent workgroups.
+long long attn_fwd_units(int B, int Hq, int N);
 
 // dtype: 0 = bf16, 1 = fp8 e4m3fn.  (d_qk, d_v) in {(128,128), (192,128)}.
 hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream);

@@ -34,7 +34,8 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, in
   if ((double)B * Hq > 2147483647.0) return MIATTN_ERR_SIZE;
   // kernels address one 128-key tile of K or V with 32-bit offsets
   if ((double)Hkv * (d_qk > d_v ? d_qk : d_v) * 2.0 * 128.0 > 2147483647.0) return MIATTN_ERR_SIZE;
-  if (miattn::attn_fwd_workgroups(B, Hq, N) <= 0) return MIATTN_ERR_SIZE;
+  const long long units = miattn::attn_fwd_units(B, Hq, N);
+  if (units <= 0 || units > 0x7fffffffLL) return MIATTN_ERR_SIZE;
   return MIATTN_OK;
 }
 
