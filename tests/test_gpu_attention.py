@@ -110,7 +110,7 @@ FULL = [("bf16_gqa_n16k", "bf16"), ("bf16_mha_n32k", "bf16"), ("fp8_mha_n1k", "f
 @pytest.mark.parametrize("name,src", FULL)
 def test_full_size_sampled_rows(require_gpu, name, src):
     """src: element type of the activations the FP8 front end reads (the
-    benchmark's step quantizes BF16 activations)."""
+    benchmark's resident FP8 inputs come from BF16 activations)."""
     w = WORKLOADS[name]
     q, k, v = make_inputs(w)
     if src == "bf16":
