@@ -615,37 +615,48 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 // A unit is a pair of query tiles of one (batch, head), the j-th from the end
 // and the j-th from the start of the causal triangle, so every unit costs about
 // the same and the workgroups finish together (separate per-tile workgroups
-// left CUs idle between workgroups and at the tail).  Workgroup w runs on XCD
-// w % 8 (round-robin dispatch); when the (batch, head) count splits evenly over
-// the 8 XCDs, XCD x takes the heads bh = x (mod 8) and its workgroups sweep one
-// head at a time, so the K/V tiles they stream are shared in that XCD's L2.
+// left CUs idle between workgroups and at the tail).  When there are no more
+// tiles than CUs, each workgroup takes a single tile instead (pairing would
+// only serialize short work).  Workgroup w runs on XCD w % 8 (round-robin
+// dispatch); when the (batch, head) count splits evenly over the 8 XCDs, XCD x
+// takes the heads bh = x (mod 8) and its workgroups sweep one head at a time,
+// so the K/V tiles they stream are shared in that XCD's L2.
 template <int DQK, int DV, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   const int nqt = (p.N + kBM - 1) / kBM;
-  const int npair = (nqt + 1) / 2;  // units per (batch, head)
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
+  const bool single = (long long)nbh * nqt <= G;  // one tile per unit
+  const int per_bh = single ? nqt : (nqt + 1) / 2;  // units per (batch, head)
   const bool by_xcd = (nbh % 8 == 0) && (G % 8 == 0);
   const int rank = by_xcd ? wg / 8 : wg, nrank = by_xcd ? G / 8 : G;
-  const int nunit = by_xcd ? (nbh / 8) * npair : nbh * npair;
+  const int nunit = by_xcd ? (nbh / 8) * per_bh : nbh * per_bh;
   // one call site (the item body is large): the two tiles of a unit are
   // iterations half = 0 (the later, heavier tile) and half = 1
   int u = rank, half = 0;
   while (u < nunit) {
-    const int bh = by_xcd ? 8 * (u / npair) + wg % 8 : u / npair;
-    const int j = u % npair;
+    const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
+    const int j = u % per_bh;
     const int qt = half == 0 ? nqt - 1 - j : j;
     if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8>(p, smem, bh, qt);
-    u += half * nrank;
-    half ^= 1;
+    if (single) {
+      u += nrank;
+    } else {
+      u += half * nrank;
+      half ^= 1;
+    }
   }
 }
 
 long long attn_fwd_units(int B, int Hq, int N) {
   const long long nqt = (N + kBM - 1) / kBM;
   return (long long)B * Hq * ((nqt + 1) / 2);
+}
+
+long long attn_fwd_tiles(int B, int Hq, int N) {
+  return (long long)B * Hq * ((N + kBM - 1) / kBM);
 }
 
 hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream) {
@@ -662,7 +673,10 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
     if (e != hipSuccess) return e;
     cu_count[dev] = n > 0 ? n : 1;
   }
-  const int grid = (int)std::min<long long>(units, cu_count[dev]);
+  const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.N);
+  // as many workgroups as CUs, or one per tile when the tiles do not fill the
+  // CUs (the kernel derives the same choice from gridDim)
+  const int grid = tiles <= cu_count[dev] ? (int)tiles : (int)std::min<long long>(units, cu_count[dev]);
   const dim3 g(grid), blk(kThreads);
   if (d_v != 128) return hipErrorInvalidValue;
   if (dtype == 0) {

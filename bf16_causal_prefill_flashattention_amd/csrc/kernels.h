@@ -21,6 +21,8 @@ struct AttnParams {
 // Work units of one attention launch (pairs of query tiles of one batch and
 // head); the launch runs min(units, CUs) persistent workgroups.
 long long attn_fwd_units(int B, int Hq, int N);
+// Query tiles (work items) of one launch.
+long long attn_fwd_tiles(int B, int Hq, int N);
 
 // dtype: 0 = bf16, 1 = fp8 e4m3fn.  (d_qk, d_v) in {(128,128), (192,128)}.
 hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream);
