@@ -579,13 +579,19 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   // Both groups run the same matrix/vector code; only where each issues its
   // share of the tile loads and which barrier waits for them differ:
   //   group A: loads(p), matrix(p) | barrier | vector(p), wait | barrier
-  //   group B: matrix(p), wait | barrier | loads(p+1), vector(p) | barrier
+  //   group B: matrix(p), wait | barrier | vector(p), loads(p+1) | barrier
+  // Group A's loads go at the start of its matrix phase for FP8 and at its end
+  // for BF16, group B's at the end of its vector phase: the positions measured
+  // fastest for each (the loads of one phase are waited for at the end of the
+  // next, when every wave has issued its share).
+  constexpr bool A_LOADS_LATE = !FP8;
   auto step = [&](int ps, auto parity) __attribute__((always_inline)) {
-    if (grp == 0) issue_step(ps);
+    if (grp == 0 && !A_LOADS_LATE) issue_step(ps);
     matrix_work(ps, parity);
+    if (grp == 0 && A_LOADS_LATE) issue_step(ps);
     barrier(grp != 0);
-    if (grp != 0) issue_step(ps + 1);
     vector_work(ps);
+    if (grp != 0) issue_step(ps + 1);
     barrier(grp == 0);
   };
   for (int ps = 0; ps <= T; ps += 2) {
