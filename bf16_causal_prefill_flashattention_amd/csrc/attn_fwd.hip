@@ -585,19 +585,27 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   // fastest for each (the loads of one phase are waited for at the end of the
   // next, when every wave has issued its share).
   constexpr bool A_LOADS_LATE = !FP8;
-  auto step = [&](int ps, auto parity) __attribute__((always_inline)) {
-    if (grp == 0 && !A_LOADS_LATE) issue_step(ps);
+  auto step = [&](int ps, auto parity, auto group) __attribute__((always_inline)) {
+    constexpr bool GA = decltype(group)::value == 0;
+    if (GA && !A_LOADS_LATE) issue_step(ps);
     matrix_work(ps, parity);
-    if (grp == 0 && A_LOADS_LATE) issue_step(ps);
-    barrier(grp != 0);
+    if (GA && A_LOADS_LATE) issue_step(ps);
+    barrier(!GA);
     vector_work(ps);
-    if (grp != 0) issue_step(ps + 1);
-    barrier(grp == 0);
+    if (!GA) issue_step(ps + 1);
+    barrier(GA);
   };
-  for (int ps = 0; ps <= T; ps += 2) {
-    step(ps, std::integral_constant<int, 0>{});
-    if (ps + 1 <= T) step(ps + 1, std::integral_constant<int, 1>{});
-  }
+  // one loop per group, so the group decisions inside a step are compile-time
+  auto run_steps = [&](auto group) __attribute__((always_inline)) {
+    for (int ps = 0; ps <= T; ps += 2) {
+      step(ps, std::integral_constant<int, 0>{}, group);
+      if (ps + 1 <= T) step(ps + 1, std::integral_constant<int, 1>{}, group);
+    }
+  };
+  if (grp == 0)
+    run_steps(std::integral_constant<int, 0>{});
+  else
+    run_steps(std::integral_constant<int, 1>{});
   if (grp == 0) barrier(false);
 
   // ---- epilogue: normalise by the row sum and store BF16
