@@ -36,14 +36,14 @@
 // barriers instead of per-instruction scheduling.
 //
 // Data movement.  K and V tiles go from HBM/L2 straight into LDS with buffer
-// loads that write LDS (no register staging): K rows are stored with a 16-byte
-// pad so that the 32 rows one MFMA operand read touches fall in distinct LDS
-// banks; V rows are stored as they are in memory with an XOR swizzle of their
-// 16-byte chunks, and the V^T operand is read with the transposing LDS reads of
-// gfx950.  Two LDS buffers each for K and V; the loads of phase 2p are waited
-// for at the end of phase 2p+1.  Rows at or beyond N load as zeros (buffer
-// bounds), so a ragged last tile needs no branches; keys >= N lie above the
-// diagonal of every valid query and are masked.
+// loads that write LDS (no register staging).  K and V rows are stored with an
+// XOR swizzle of their 16-byte chunks so that the rows one operand read
+// touches fall in distinct LDS banks; the V^T operand is read with the
+// transposing LDS reads of gfx950.  Two LDS buffers each for K and V; the loads
+// of phase 2p are waited for at the end of phase 2p+1.  Rows at or beyond N,
+// and whole tiles past the last one a workgroup needs, load as zeros (buffer
+// bounds), so ragged tiles and the loads of the final steps need no branches;
+// keys >= N lie above the diagonal of every valid query and are masked.
 //
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
@@ -79,12 +79,14 @@ struct Cfg {
   static constexpr int VROW = DV * EB;       // bytes of one V row
   static constexpr int KCH = KROW / 16;      // 16-byte chunks per K row
   static constexpr int VCH = VROW / 16;      // 16-byte chunks per V row
-  static constexpr int KPITCH = KROW + 16;   // padded LDS pitch of a K row
-  static constexpr int K_TILE = BN * KPITCH;
+  // K rows are stored unpadded with their 16-byte chunks XOR-swizzled inside
+  // groups of KG chunks (k_swizzle), V rows likewise (v_swizzle)
+  static constexpr int KG = KCH % 16 == 0 ? 16 : (KCH % 8 == 0 ? 8 : 4);
+  static constexpr int K_TILE = BN * KROW;
   static constexpr int V_TILE = BN * VROW;
-  static constexpr int K_BLOCKS = BN * (KCH + 1) / 64;  // 1 KB LDS-load blocks per K tile (pad chunks included)
+  static constexpr int K_BLOCKS = BN * KCH / 64;  // 1 KB LDS-load blocks per K tile
   static constexpr int V_BLOCKS = BN * VCH / 64;
-  static constexpr int K_PER_WAVE = (K_BLOCKS + kWaves - 1) / kWaves;
+  static constexpr int K_PER_WAVE = K_BLOCKS / kWaves;
   static constexpr int V_PER_WAVE = V_BLOCKS / kWaves;
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
   static constexpr int LDS_BYTES = 2 * V_TILE + 2 * K_TILE;
@@ -95,7 +97,7 @@ struct Cfg {
   // FP8 probabilities are written as e4m3 codes straight from the log2-domain
   // score ("lean P"): the code of 2^x is about 8x + 56, exact at integer x.
   static constexpr bool LEAN_P = FP8;
-  static_assert((BN * (KCH + 1)) % 64 == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks");
+  static_assert(K_BLOCKS % kWaves == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks per wave");
   static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
 };
 
@@ -109,6 +111,29 @@ __device__ __forceinline__ int v_swizzle(int key) {
     return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2);
   else
     return (key & 3) << 2;
+}
+
+// XOR applied inside a group of KG 16-byte chunks of K row `row` in LDS.  The
+// 16 lanes that one quarter of a 16-byte operand read serves (rows r..r+15, one
+// chunk) then fall in 16 distinct groups of four banks: 128-byte rows (FP8,
+// d=128) alternate two 8-chunk bank halves, so the swizzle takes rows in
+// pairs; 256-byte rows (BF16) start in the same bank, so every row gets its
+// own; 192-byte rows (FP8 MLA) cycle four 4-chunk groups; 384-byte rows (BF16
+// MLA) alternate halves like 128-byte ones.
+template <class C>
+__device__ __forceinline__ int k_swizzle(int row) {
+  if constexpr (C::KROW == 256)
+    return row & 15;
+  else if constexpr (C::KROW == 192)
+    return (row >> 2) & 3;
+  else
+    return (row >> 1) & 7;
+}
+// LDS position (chunk index within the row) of logical chunk `ch` of K row `row`
+// (an involution: it also maps a position back to its logical chunk)
+template <class C>
+__device__ __forceinline__ int k_chunk_pos(int row, int ch) {
+  return (ch & ~(C::KG - 1)) | ((ch ^ k_swizzle<C>(row)) & (C::KG - 1));
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -228,7 +253,7 @@ template <class C, bool FP8, int DQK, int DV>
 struct Wave {
   static constexpr int NBLK = C::NBLK;
   // per-lane LDS byte offsets (relative to a buffer)
-  int k_lane;               // K operand: row l % 32, k-half
+  int k_lane[C::KG];        // K operand: row l % 32, chunk group position (k-half folded in)
   int v_lane[DV / 32];      // V^T operand per 32-channel block
   uint32_t k_dma[C::K_PER_WAVE];
   uint32_t v_dma[C::V_PER_WAVE];
@@ -281,7 +306,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   Wave<C, FP8, DQK, DV> wv;
 
   // ---- per-lane LDS offsets of the operand reads
-  wv.k_lane = l32 * C::KPITCH + hl * (FP8 ? 32 : 16);
+  // chunk ct of a K-operand read is logical chunk ct + (2 or 1) * hl of the
+  // lane's row l % 32 (the rows of block blk are l % 32 + 32 blk, same swizzle)
+#pragma unroll
+  for (int ct = 0; ct < C::KG; ++ct)
+    wv.k_lane[ct] = l32 * C::KROW + 16 * ((ct ^ (hl * (FP8 ? 2 : 1)) ^ k_swizzle<C>(l32)) & (C::KG - 1));
   {
     const int grp16 = lane >> 4, s16 = lane & 15;
     const int lhl = grp16 >> 1, gc = grp16 & 1;
@@ -308,8 +337,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 #pragma unroll
   for (int i = 0; i < C::K_PER_WAVE; ++i) {
     const int blk = w + kWaves * i;
-    const int pos = 64 * blk + lane, row = pos / (C::KCH + 1), ch = pos % (C::KCH + 1);
-    wv.k_dma[i] = (ch < C::KCH) ? (uint32_t)row * k_pitch + 16u * ch : 0x80000000u;  // pad chunks load zeros
+    const int pos = 64 * blk + lane, row = pos / C::KCH, slot = pos % C::KCH;
+    wv.k_dma[i] = (uint32_t)row * k_pitch + 16u * k_chunk_pos<C>(row, slot);
   }
 #pragma unroll
   for (int i = 0; i < C::V_PER_WAVE; ++i) {
@@ -323,18 +352,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   // tiles this wave needs: keys up to its last valid query
   const int Tw = qw0 < N ? (min(qw0 + 31, N - 1) / BN + 1) : 0;
 
+  // tiles at or beyond T load with an empty range (zeros, no memory access), so
+  // the loads need no branches
+  const int krows_end = min(N, T * BN);
   auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
     const int kb = t * BN;
-    const i32x4 rk = rsrc_words(K + (size_t)kb * k_pitch, (uint32_t)min(N - kb, BN) * k_pitch);
+    const int rows = max(0, min(krows_end - kb, BN));
+    const i32x4 rk = rsrc_words(K + (size_t)min(kb, krows_end) * k_pitch, (uint32_t)rows * k_pitch);
 #pragma unroll
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
-      if (blk < C::K_BLOCKS) load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
+      load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
     }
   };
   auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
     const int kb = t * BN;
-    const i32x4 rv = rsrc_words(V + (size_t)kb * v_pitch, (uint32_t)min(N - kb, BN) * v_pitch);
+    const int rows = max(0, min(krows_end - kb, BN));
+    const i32x4 rv = rsrc_words(V + (size_t)min(kb, krows_end) * v_pitch, (uint32_t)rows * v_pitch);
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
@@ -343,8 +377,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   };
   // loads of step p: K tile p+1 and V tile p
   auto issue_step = [&](int pstep) __attribute__((always_inline)) {
-    if (pstep + 1 < T) issue_k(pstep + 1, (pstep + 1) & 1);
-    if (pstep < T) issue_v(pstep, pstep & 1);
+    issue_k(pstep + 1, (pstep + 1) & 1);
+    issue_v(pstep, pstep & 1);
   };
 
   // ---- Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16),
@@ -409,12 +443,16 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
       }
     } else {
       const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
+      const uint8_t* row = kb + blk * 32 * C::KROW;
       if constexpr (FP8) {
-        const uint8_t* src = kb + blk * 32 * C::KPITCH + kk * 64;
-        const i32x4 lo = lds_load16(src), hi = lds_load16(src + 16);
+        // logical chunks 4kk + 2hl + {0, 1}
+        const int c0 = 4 * kk, c1 = 4 * kk + 1;
+        const i32x4 lo = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
+        const i32x4 hi = lds_load16(row + wv.k_lane[c1 & (C::KG - 1)] + 16 * (c1 & ~(C::KG - 1)));
         a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
-        a = lds_load16(kb + blk * 32 * C::KPITCH + kk * 32);
+        const int c0 = 2 * kk;  // logical chunk 2kk + hl
+        a = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
       }
     }
     return a;
@@ -473,7 +511,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   auto matrix_work = [&](int pstep, auto parity) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parity)::value;  // pstep & 1
     const uint8_t* vb = Vs + (1 - PAR) * C::V_TILE;       // V tile pstep-1
-    const uint8_t* kb = Ks + PAR * C::K_TILE + wv.k_lane;  // K tile pstep
+    const uint8_t* kb = Ks + PAR * C::K_TILE;  // K tile pstep
     // One instruction sequence for every step the wave takes part in (a single
     // variant keeps the register allocation tight): at step 0 the P.V product
     // multiplies zero probabilities with a zero-filled V buffer, and at step Tw
