@@ -173,6 +173,22 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
                (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 
+// Bytes of rows [kb, min(kb + BN, end)) of a tile at pitch `pitch`, on the
+// scalar unit (left to itself the compiler clamps with a vector med3 and a
+// vector multiply, then moves the result back to a scalar register: a chain of
+// dependent instructions in front of every tile load).
+__device__ __forceinline__ uint32_t tile_bytes(int end, int kb, int bn, uint32_t pitch) {
+  int r;
+  asm("s_sub_i32 %0, %1, %2\n\t"
+      "s_min_i32 %0, %0, %3\n\t"
+      "s_max_i32 %0, %0, 0\n\t"
+      "s_mul_i32 %0, %0, %4"
+      : "=&s"(r)
+      : "s"(end), "s"(kb), "s"(bn), "s"(pitch)
+      : "scc");
+  return (uint32_t)r;
+}
+
 // Workgroup barrier that also orders every memory access around it in the
 // compiler; with wait_loads the wave first waits for its own outstanding
 // global/buffer loads (including the LDS-writing ones).
@@ -354,11 +370,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 
   // tiles at or beyond T load with an empty range (zeros, no memory access), so
   // the loads need no branches
-  const int krows_end = min(N, T * BN);
+  // (read-first-lane: keeps the load-range arithmetic on the scalar unit)
+  const int krows_end = __builtin_amdgcn_readfirstlane(min(N, T * BN));
   auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
     const int kb = t * BN;
-    const int rows = max(0, min(krows_end - kb, BN));
-    const i32x4 rk = rsrc_words(K + (size_t)min(kb, krows_end) * k_pitch, (uint32_t)rows * k_pitch);
+    const i32x4 rk = rsrc_words(K + (size_t)min(kb, krows_end) * k_pitch, tile_bytes(krows_end, kb, BN, k_pitch));
 #pragma unroll
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
@@ -367,8 +383,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   };
   auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
     const int kb = t * BN;
-    const int rows = max(0, min(krows_end - kb, BN));
-    const i32x4 rv = rsrc_words(V + (size_t)min(kb, krows_end) * v_pitch, (uint32_t)rows * v_pitch);
+    const i32x4 rv = rsrc_words(V + (size_t)min(kb, krows_end) * v_pitch, tile_bytes(krows_end, kb, BN, v_pitch));
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
