@@ -9,7 +9,10 @@ B * Hq * N^2 * (d_qk + d_v), the attention kernel alone as the metric defines
 it.  The FP8 front end (per-head amax/448 quantization of the BF16 activations
 Q, K, V) produces those resident inputs before the timed region and is timed
 on its own under ``front_end``.  The BF16 point of the same metric (BF16,
-d = 128, N = 32K) is reported in the same line under ``bf16``.
+d = 128, N = 32K) is reported in the same line under ``bf16``, and one chunk
+of a chunked prefill (the last 8192 positions of the same 32K FP8 sequence
+against all 32768 keys, with the LSE output) under ``chunk``, its FLOPs
+counted the same way: B * Hq * (2 Nq Nk - Nq^2) * (d_qk + d_v).
 
 ``roofline`` describes the attention kernel (the dominant one): its algorithmic
 FLOPs per launch divided by its average launch duration, measured with HIP
@@ -127,8 +130,53 @@ def run_gpu(w, steps: int, warmup: int):
     return ms_per_step, attn_ms, front_ms
 
 
-def roofline(w, attn_ms):
-    flops = w.causal_flops
+def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
+    """Causal FLOPs of a chunk, in the convention of B * Hq * N^2 * (d_qk + d_v)
+    (which is the Nq == Nk case): 2 * (visible query-key pairs) * (d_qk + d_v)
+    with the pairs counted as Nq * Nk - Nq^2 / 2."""
+    return float(B) * Hq * (2.0 * Nq * Nk - float(Nq) ** 2) * (d_qk + d_v)
+
+
+def run_chunk(w, Nq: int, steps: int, warmup: int):
+    """Time attn_fwd_chunk (with LSE) for the last Nq positions of workload w's
+    FP8 sequence; inputs quantized by the library and resident in HBM.
+    Returns (wall ms per step, per-launch event ms)."""
+    import torch
+
+    import bf16_causal_prefill_flashattention_amd as miattn
+    from bf16_causal_prefill_flashattention_amd.inputs import make_qkv
+
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w)
+    q = q[:, w.N - Nq:].contiguous()
+    q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))
+    (cq, sq), (ck, sk), (cv, sv) = (miattn.attn_quantize_fp8(t) for t in (q, k, v))
+    del q, k, v
+    out = torch.empty((w.B, Nq, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        miattn.attn_fwd_chunk(cq, ck, cv, sq, sk, sv, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
+
+
+def roofline(w, attn_ms, flops=None):
+    flops = w.causal_flops if flops is None else flops
     avg_s = sum(attn_ms) / len(attn_ms) * 1e-3
     achieved = flops / avg_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -202,6 +250,8 @@ def main(argv=None):
     ap.add_argument("--bf16-workload", default="bf16_mha_n32k")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--chunk-queries", type=int, default=8192)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the warmup, run one plain elementwise copy (torch.neg) that reads and writes "
@@ -261,6 +311,18 @@ def main(argv=None):
             "ms_per_step": round(msb, 4),
             "roofline": roofline(wb, attn_b),
         }
+    if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
+        Nq = args.chunk_queries
+        msc, attn_c = run_chunk(w, Nq, args.steps, args.warmup)
+        fl = chunk_flops(w.B, w.Hq, Nq, w.N, w.d_qk, w.d_v)
+        rec["chunk"] = {
+            "workload": f"{w.name} chunk: last {Nq} positions against {w.N} keys, LSE written",
+            "Nq": Nq, "Nk": w.N,
+            "value": round(fl / (msc * 1e-3) / 1e12, 1),
+            "ms_per_step": round(msc, 4),
+            "roofline": roofline(w, attn_c, fl),
+        }
+        rec["chunk"]["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     rec["kernel_source_hash"] = kernel_source_hash()

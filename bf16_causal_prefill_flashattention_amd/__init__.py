@@ -9,6 +9,8 @@ a tensor is not on a GPU, the call raises.
 Entry points (same names as the C ABI):
 
 * ``attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None)``
+* ``attn_fwd_chunk(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None,
+  lse=None, with_lse=True, softmax_scale=None)``
 * ``attn_quantize_fp8(x, hadamard=False, out=None, scale=None)``
 * ``attn_status_string(status)``, ``attn_version()``
 """
@@ -20,6 +22,7 @@ import os
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_chunk",
     "attn_quantize_fp8",
     "attn_status_string",
     "attn_version",
@@ -63,6 +66,9 @@ def load_library() -> ctypes.CDLL:
     vp, ci, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, vp]
     lib.attn_fwd.restype = ci
+    lib.attn_fwd_chunk.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp,
+                                   ctypes.c_float, vp]
+    lib.attn_fwd_chunk.restype = ci
     lib.attn_quantize_fp8.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8.restype = ci
     lib.attn_status_string.argtypes = [ci]
@@ -108,20 +114,17 @@ def _as_codes(name, t):
     raise TypeError(f"{name} must be uint8 or float8_e4m3fn codes for the FP8 path")
 
 
-def attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None):
-    """Causal attention forward.  q [B,N,Hq,d_qk], k [B,N,Hkv,d_qk],
-    v [B,N,Hkv,d_v] (contiguous BSHD, on one GPU).  BF16 tensors select the
-    BF16 path; uint8 / float8_e4m3fn codes select the FP8 path, which needs
-    fp32 scales q_scale [B,Hq], k_scale [B,Hkv], v_scale [B,Hkv].  Returns
-    ``out`` (bf16 [B,N,Hq,d_v]), allocated if not given."""
+def _attn_args(q, k, v, q_scale, k_scale, v_scale):
+    """Check q [B,Nq,Hq,d_qk], k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] and the FP8
+    scales; returns (q, k, v, dtype code, scale pointers, sizes)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu_contig(name, t)
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, N, H, d]")
-    B, N, Hq, dqk = q.shape
-    Hkv, dv = k.shape[2], v.shape[3]
-    if tuple(k.shape) != (B, N, Hkv, dqk) or tuple(v.shape[:3]) != (B, N, Hkv):
+    B, Nq, Hq, dqk = q.shape
+    Nk, Hkv, dv = k.shape[1], k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, Nk, Hkv, dqk) or tuple(v.shape[:3]) != (B, Nk, Hkv):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if q.dtype == torch.bfloat16:
         if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
@@ -141,12 +144,29 @@ def attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None):
                 raise ValueError(f"{name} must be float32 {shape}")
             scales.append(s)
         ptr_s = [s.data_ptr() for s in scales]
+    return q, k, v, dtype, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv)
+
+
+def _out_tensor(out, q, B, Nq, Hq, dv):
+    torch = _torch()
     if out is None:
-        out = torch.empty((B, N, Hq, dv), dtype=torch.bfloat16, device=q.device)
-    else:
-        _check_gpu_contig("out", out)
-        if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, N, Hq, dv):
-            raise ValueError("out must be bfloat16 [B, N, Hq, d_v]")
+        return torch.empty((B, Nq, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _check_gpu_contig("out", out)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Nq, Hq, dv):
+        raise ValueError(f"out must be bfloat16 {(B, Nq, Hq, dv)}")
+    return out
+
+
+def attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None):
+    """Causal attention forward.  q [B,N,Hq,d_qk], k [B,N,Hkv,d_qk],
+    v [B,N,Hkv,d_v] (contiguous BSHD, on one GPU).  BF16 tensors select the
+    BF16 path; uint8 / float8_e4m3fn codes select the FP8 path, which needs
+    fp32 scales q_scale [B,Hq], k_scale [B,Hkv], v_scale [B,Hkv].  Returns
+    ``out`` (bf16 [B,N,Hq,d_v]), allocated if not given."""
+    q, k, v, dtype, ptr_s, (B, N, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale)
+    if Nk != N:
+        raise ValueError(f"q and k must have the same length (got {N} and {Nk}); see attn_fwd_chunk")
+    out = _out_tensor(out, q, B, N, Hq, dv)
     st = load_library().attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, N, dqk, dv, dtype,
         ptr_s[0], ptr_s[1], ptr_s[2], _stream_handle(q.device),
@@ -154,6 +174,35 @@ def attn_fwd(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None):
     if st != 0:
         raise MiattnError("attn_fwd", st)
     return out
+
+
+def attn_fwd_chunk(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None, lse=None, with_lse=True,
+                   softmax_scale=None):
+    """One chunk of a chunked causal prefill: q [B,Nq,Hq,d_qk] holds the last
+    Nq positions of a sequence whose first Nk >= Nq keys and values are
+    k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v]; query row i sees keys
+    j <= i + Nk - Nq.  Dtypes and scales as for ``attn_fwd``.
+    ``softmax_scale``: tau (default 1/sqrt(d_qk)).  Returns ``(out, lse)``:
+    out bf16 [B,Nq,Hq,d_v]; lse fp32 [B,Hq,Nq], the natural-log sum of
+    exp(tau <q_i, k_j>) over the visible keys, or None when ``with_lse`` is
+    false and no ``lse`` tensor is given."""
+    torch = _torch()
+    q, k, v, dtype, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale)
+    out = _out_tensor(out, q, B, Nq, Hq, dv)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_gpu_contig("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError(f"lse must be float32 {(B, Hq, Nq)}")
+    st = load_library().attn_fwd_chunk(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, dqk, dv, dtype, ptr_s[0], ptr_s[1], ptr_s[2],
+        0.0 if softmax_scale is None else float(softmax_scale), _stream_handle(q.device),
+    )
+    if st != 0:
+        raise MiattnError("attn_fwd_chunk", st)
+    return out, lse
 
 
 def attn_quantize_fp8(x, hadamard: bool = False, out=None, scale=None):

@@ -11,6 +11,12 @@
 // products accumulate in FP32 ([P1] "ZYFA's performance and accuracy data";
 // [P3] "为什么 FP8 注意力在 MI355X 上表现不佳？").  Output is BF16.
 //
+// Queries may be the last Nq positions of a longer key sequence (Nq <= Nk: one
+// chunk of a chunked prefill against the keys and values before it); query row
+// i then sits at position i + Nk - Nq.  Optionally the natural-log sum of exp
+// of each query's scaled scores (LSE) is written, which is what combining the
+// results of separate key ranges needs.
+//
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
 // (batch, query head); each wave owns 32 queries.  Key tiles hold 128 keys
 // (FP8) or 64 keys (BF16); a wave skips the tiles wholly above its queries and
@@ -40,10 +46,11 @@
 // XOR swizzle of their 16-byte chunks so that the rows one operand read
 // touches fall in distinct LDS banks; the V^T operand is read with the
 // transposing LDS reads of gfx950.  Two LDS buffers each for K and V; the loads
-// of phase 2p are waited for at the end of phase 2p+1.  Rows at or beyond N,
-// and whole tiles past the last one a workgroup needs, load as zeros (buffer
-// bounds), so ragged tiles and the loads of the final steps need no branches;
-// keys >= N lie above the diagonal of every valid query and are masked.
+// of phase 2p are waited for at the end of phase 2p+1.  Rows at or beyond Nq
+// (queries) or Nk (keys), and whole tiles past the last one a workgroup needs,
+// load as zeros (buffer bounds), so ragged tiles and the loads of the final
+// steps need no branches; keys >= Nk lie above the diagonal of every valid
+// query and are masked.
 //
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
@@ -296,21 +303,22 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int grp = w >> 2;  // 0: matrix work on even phases, 1: on odd phases
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int off = Nk - Nq;  // position of query row 0 in the key sequence
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / (p.Hq / p.Hkv);
   const int q0 = qt * kBM;
   // SIMD s runs waves s (group 0) and s + 4 (group 1); they own query blocks
   // 2s and 2s + 1, so both groups have work on the diagonal tiles.
   const int qblk = 2 * (w & 3) + grp;
   const int qw0 = q0 + 32 * qblk;  // first query of this wave
-  const int my_q = qw0 + l32;      // query owned by this lane
+  const int my_q = qw0 + l32;      // query row owned by this lane (position my_q + off)
 
   const uint32_t q_pitch = (uint32_t)p.Hq * C::KROW;  // bytes between consecutive positions
   const uint32_t k_pitch = (uint32_t)p.Hkv * C::KROW;
   const uint32_t v_pitch = (uint32_t)p.Hkv * C::VROW;
-  const uint8_t* Q = static_cast<const uint8_t*>(p.q) + ((size_t)b * N * p.Hq + h) * C::KROW;
-  const uint8_t* K = static_cast<const uint8_t*>(p.k) + ((size_t)b * N * p.Hkv + g) * C::KROW;
-  const uint8_t* V = static_cast<const uint8_t*>(p.v) + ((size_t)b * N * p.Hkv + g) * C::VROW;
+  const uint8_t* Q = static_cast<const uint8_t*>(p.q) + ((size_t)b * Nq * p.Hq + h) * C::KROW;
+  const uint8_t* K = static_cast<const uint8_t*>(p.k) + ((size_t)b * Nk * p.Hkv + g) * C::KROW;
+  const uint8_t* V = static_cast<const uint8_t*>(p.v) + ((size_t)b * Nk * p.Hkv + g) * C::VROW;
 
   float c = p.sm_scale_log2;  // log2-domain score scale (dequantisation folded in for FP8)
   float sv = 1.f;
@@ -363,15 +371,15 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
     wv.v_dma[i] = (uint32_t)key * v_pitch + 16u * (slot ^ v_swizzle<FP8>(key));
   }
 
-  const int kend = min(q0 + kBM, N);
-  const int T = (kend + BN - 1) / BN;  // key tiles of the workgroup
-  // tiles this wave needs: keys up to its last valid query
-  const int Tw = qw0 < N ? (min(qw0 + 31, N - 1) / BN + 1) : 0;
+  const int kend = min(q0 + kBM, Nq) + off;  // keys visible to the workgroup's last query, plus one
+  const int T = (kend + BN - 1) / BN;        // key tiles of the workgroup
+  // tiles this wave needs: keys up to the position of its last valid query
+  const int Tw = qw0 < Nq ? ((min(qw0 + 31, Nq - 1) + off) / BN + 1) : 0;
 
   // tiles at or beyond T load with an empty range (zeros, no memory access), so
   // the loads need no branches
   // (read-first-lane: keeps the load-range arithmetic on the scalar unit)
-  const int krows_end = __builtin_amdgcn_readfirstlane(min(N, T * BN));
+  const int krows_end = __builtin_amdgcn_readfirstlane(min(Nk, T * BN));
   auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
     const int kb = t * BN;
     const i32x4 rk = rsrc_words(K + (size_t)min(kb, krows_end) * k_pitch, tile_bytes(krows_end, kb, BN, k_pitch));
@@ -399,8 +407,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   // ---- Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16),
   // lane half hl holds 8 of them; FP8: k-step kk = channels [64kk, 64kk+64), 32 each.
   {
-    const uint32_t rows = (uint32_t)max(0, min(32, N - qw0));
-    const auto rq = make_rsrc(Q + (size_t)min(qw0, N) * q_pitch, rows * q_pitch);
+    const uint32_t rows = (uint32_t)max(0, min(32, Nq - qw0));
+    const auto rq = make_rsrc(Q + (size_t)min(qw0, Nq) * q_pitch, rows * q_pitch);
 #pragma unroll
     for (int kk = 0; kk < C::QK_STEPS; ++kk) {
       if constexpr (FP8) {
@@ -539,10 +547,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   auto vector_work = [&](int pstep) __attribute__((always_inline)) {
     if (pstep < 0 || pstep >= Tw) return;
     const int kb = pstep * BN;
-    if (kb + BN - 1 > qw0) {  // the tile crosses this wave's diagonal: mask keys above each query
+    if (kb + BN - 1 > qw0 + off) {  // the tile crosses this wave's diagonal: mask keys above each query
       // key offset k of register r is visible iff k <= lim; the sign of lim - k
       // selects -inf bit by bit (no per-element compare masks held in SGPRs)
-      const int lim = my_q - kb - 4 * hl;
+      const int lim = my_q + off - kb - 4 * hl;
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
@@ -663,8 +671,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 
   // ---- epilogue: normalise by the row sum and store BF16
   const float inv = sv / wv.st.l4[0];
-  if (my_q < N) {
-    __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * N + my_q) * p.Hq + h) * DV;
+  if (my_q < Nq) {
+    // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
+    // log2 sum_j 2^x_j = m - SHIFT + log2(l); lanes l and l + 32 share a query
+    if (p.lse != nullptr && hl == 0)
+      p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(wv.st.l4[0])) * 0.69314718055994531f;
+    __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * Nq + my_q) * p.Hq + h) * DV;
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) {
 #pragma unroll
@@ -692,7 +704,7 @@ template <int DQK, int DV, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-  const int nqt = (p.N + kBM - 1) / kBM;
+  const int nqt = (p.Nq + kBM - 1) / kBM;
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
   const bool single = (long long)nbh * nqt <= G;  // one tile per unit
@@ -717,17 +729,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-long long attn_fwd_units(int B, int Hq, int N) {
-  const long long nqt = (N + kBM - 1) / kBM;
+long long attn_fwd_units(int B, int Hq, int Nq) {
+  const long long nqt = (Nq + kBM - 1) / kBM;
   return (long long)B * Hq * ((nqt + 1) / 2);
 }
 
-long long attn_fwd_tiles(int B, int Hq, int N) {
-  return (long long)B * Hq * ((N + kBM - 1) / kBM);
+long long attn_fwd_tiles(int B, int Hq, int Nq) {
+  return (long long)B * Hq * ((Nq + kBM - 1) / kBM);
 }
 
 hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hipStream_t stream) {
-  const long long units = attn_fwd_units(p.B, p.Hq, p.N);
+  if (p.Nq < 1 || p.Nk < p.Nq) return hipErrorInvalidValue;
+  const long long units = attn_fwd_units(p.B, p.Hq, p.Nq);
   if (units <= 0 || units > 0x7fffffffLL) return hipErrorInvalidValue;
   static int cu_count[64];  // per device, filled on first use
   int dev = 0;
@@ -740,7 +753,7 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
     if (e != hipSuccess) return e;
     cu_count[dev] = n > 0 ? n : 1;
   }
-  const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.N);
+  const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.Nq);
   // as many workgroups as CUs, or one per tile when the tiles do not fill the
   // CUs (the kernel derives the same choice from gridDim)
   const int grid = tiles <= cu_count[dev] ? (int)tiles : (int)std::min<long long>(units, cu_count[dev]);

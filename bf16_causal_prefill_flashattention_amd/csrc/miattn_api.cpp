@@ -17,26 +17,50 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool supported_dims(int d_qk, int d_v) { return d_v == 128 && (d_qk == 128 || d_qk == 192); }
 
 // Validation touches no device state, so a rejected call enqueues nothing.
-int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
-                      int d_qk, int d_v, int dtype, const float* qs, const float* ks, const float* vs) {
+int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, const float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d_qk, int d_v, int dtype, const float* qs, const float* ks,
+                      const float* vs) {
   if (dtype != MIATTN_DTYPE_BF16 && dtype != MIATTN_DTYPE_FP8_E4M3) return MIATTN_ERR_DTYPE;
-  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return MIATTN_ERR_SIZE;
+  if (B < 0 || Nq < 0 || Nk < Nq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return MIATTN_ERR_SIZE;
   if (!supported_dims(d_qk, d_v)) return MIATTN_ERR_SHAPE;
-  if (B == 0 || N == 0) return MIATTN_OK;  // empty: pointers are not dereferenced
+  if (B == 0 || Nq == 0) return MIATTN_OK;  // empty: pointers are not dereferenced
   if (!q || !k || !v || !out) return MIATTN_ERR_NULL;
   if (dtype == MIATTN_DTYPE_FP8_E4M3 && (!qs || !ks || !vs)) return MIATTN_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return MIATTN_ERR_ALIGN;
   if (dtype == MIATTN_DTYPE_FP8_E4M3 && (!aligned(qs, 4) || !aligned(ks, 4) || !aligned(vs, 4)))
     return MIATTN_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return MIATTN_ERR_ALIGN;
   // every element offset must fit in 63 bits and the grid in a 31-bit count
-  const double elems = (double)B * (double)N * (double)Hq * (double)(d_qk > d_v ? d_qk : d_v);
-  if (elems > 9.0e18) return MIATTN_ERR_SIZE;
+  const double dmax = (double)(d_qk > d_v ? d_qk : d_v);
+  if ((double)B * (double)Nk * (double)Hq * dmax > 9.0e18) return MIATTN_ERR_SIZE;
   if ((double)B * Hq > 2147483647.0) return MIATTN_ERR_SIZE;
   // kernels address one 128-key tile of K or V with 32-bit offsets
-  if ((double)Hkv * (d_qk > d_v ? d_qk : d_v) * 2.0 * 128.0 > 2147483647.0) return MIATTN_ERR_SIZE;
-  const long long units = miattn::attn_fwd_units(B, Hq, N);
+  if ((double)Hkv * dmax * 2.0 * 128.0 > 2147483647.0) return MIATTN_ERR_SIZE;
+  const long long units = miattn::attn_fwd_units(B, Hq, Nq);
   if (units <= 0 || units > 0x7fffffffLL) return MIATTN_ERR_SIZE;
   return MIATTN_OK;
+}
+
+int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                 const float* v_scale, double tau, void* stream) {
+  miattn::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.sm_scale_log2 = (float)(1.4426950408889634 * tau);  // log2-domain softmax scale
+  const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
 
 int validate_quantize(const void* x, int x_dtype, void* y, float* scale, int B, int H, int N, int d,
@@ -68,35 +92,35 @@ const char* attn_status_string(int status) {
   switch (status) {
     case MIATTN_OK: return "success";
     case MIATTN_ERR_NULL: return "a required pointer is NULL";
-    case MIATTN_ERR_SIZE: return "invalid size (negative, zero head count, Hq not a multiple of Hkv, or too large)";
+    case MIATTN_ERR_SIZE: return "invalid size (negative, zero head count, Hq not a multiple of Hkv, Nq > Nk, or too large)";
     case MIATTN_ERR_SHAPE: return "unsupported head dimensions (need (128,128) or (192,128); Hadamard needs d=128)";
     case MIATTN_ERR_DTYPE: return "unknown dtype, source type or flag value";
     case MIATTN_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
-    case MIATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales 4-byte alignment)";
+    case MIATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales and lse 4-byte alignment)";
+    case MIATTN_ERR_VALUE: return "invalid scalar argument (softmax scale must be finite and positive, or 0)";
     default: return "unknown status code";
   }
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d_qk,
              int d_v, int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* stream) {
-  const int st = validate_attn_fwd(q, k, v, out, B, Hq, Hkv, N, d_qk, d_v, dtype, q_scale, k_scale, v_scale);
+  const int st =
+      validate_attn_fwd(q, k, v, out, nullptr, B, Hq, Hkv, N, N, d_qk, d_v, dtype, q_scale, k_scale, v_scale);
   if (st != MIATTN_OK || B == 0 || N == 0) return st;
-  miattn::AttnParams p;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.out = out;
-  p.q_scale = q_scale;
-  p.k_scale = k_scale;
-  p.v_scale = v_scale;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.N = N;
-  // log2-domain softmax scale: tau * log2(e), tau = 1/sqrt(d_qk)
-  p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_qk));
-  const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+  return run_attn_fwd(q, k, v, out, nullptr, B, Hq, Hkv, N, N, d_qk, d_v, dtype, q_scale, k_scale, v_scale,
+                      1.0 / std::sqrt((double)d_qk), stream);
+}
+
+int attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                   const float* v_scale, float softmax_scale, void* stream) {
+  if (!(softmax_scale == 0.0f || (std::isfinite(softmax_scale) && softmax_scale > 0.0f))) return MIATTN_ERR_VALUE;
+  const int st =
+      validate_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, dtype, q_scale, k_scale, v_scale);
+  if (st != MIATTN_OK || B == 0 || Nq == 0) return st;
+  const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
+  return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, dtype, q_scale, k_scale, v_scale, tau,
+                      stream);
 }
 
 int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,

@@ -20,7 +20,7 @@
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 1
+#define MIATTN_ABI_VERSION 2
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -33,11 +33,12 @@ extern "C" {
 /* Status codes (0 = success, negative = error; nothing was enqueued). */
 #define MIATTN_OK 0
 #define MIATTN_ERR_NULL (-1)     /* a required pointer is NULL */
-#define MIATTN_ERR_SIZE (-2)     /* a size is negative, zero where it may not be, Hq % Hkv != 0, or too large */
+#define MIATTN_ERR_SIZE (-2)     /* a size is negative, zero where it may not be, Hq % Hkv != 0, Nq > Nk, or too large */
 #define MIATTN_ERR_SHAPE (-3)    /* unsupported head dimensions, or Hadamard with d != 128 */
 #define MIATTN_ERR_DTYPE (-4)    /* unknown dtype / source type code, or a flag outside {0, 1} */
 #define MIATTN_ERR_HIP (-5)      /* the HIP runtime reported an error when enqueuing */
-#define MIATTN_ERR_ALIGN (-6)    /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
+#define MIATTN_ERR_ALIGN (-6)    /* a tensor pointer is not 16-byte aligned (scales, lse: 4-byte) */
+#define MIATTN_ERR_VALUE (-7)    /* a scalar argument is out of range (softmax scale) */
 
 /* Causal forward attention, O = softmax(tau * Q K^T + causal mask) V.
  *
@@ -73,6 +74,37 @@ extern "C" {
  * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d_qk,
              int d_v, int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* stream);
+
+/* One chunk of a chunked causal prefill: the last Nq positions of a sequence
+ * attend to its first Nk keys and values (Nq <= Nk), with an optional
+ * log-sum-exp output and an explicit softmax scale.
+ *
+ * Defines: the same causal attention as attn_fwd (see there for the pages'
+ * passages), with the queries placed after a prefix of Nk - Nq keys that they
+ * all see.  The pages stop at plain causal prefill; this entry point is the
+ * step beside it that lets a long prefill run in chunks against the keys and
+ * values already computed, and lets partial results over separate key ranges
+ * be combined through their log-sum-exp.
+ *
+ * Layout (contiguous BSHD, as attn_fwd):
+ *   q   [B, Nq, Hq,  d_qk]  dtype       query row i is sequence position i + Nk - Nq
+ *   k   [B, Nk, Hkv, d_qk]  dtype
+ *   v   [B, Nk, Hkv, d_v]   dtype
+ *   out [B, Nq, Hq,  d_v]   bfloat16 (written)
+ *   lse [B, Hq, Nq]         fp32 (written unless NULL):
+ *        lse[b, h, i] = ln sum_{j <= i + Nk - Nq} exp(tau * <q_i, k_j>),
+ *        on the dequantized inputs for FP8.
+ * Query row i attends to keys j <= i + Nk - Nq.  Nq == Nk with lse == NULL and
+ * softmax_scale == 0 is exactly attn_fwd.
+ * softmax_scale: tau; 0 selects 1 / sqrt(d_qk); otherwise it must be finite
+ * and positive (else MIATTN_ERR_VALUE).
+ * Scales, dtypes, head dimensions, stream and determinism as for attn_fwd.
+ * Sizes: B >= 0, 0 <= Nq <= Nk, Hq >= 1, Hkv >= 1, Hq % Hkv == 0; B == 0 or
+ * Nq == 0 is an empty call (success, nothing enqueued).
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                   const float* v_scale, float softmax_scale, void* stream);
 
 /* Per-(batch, head) FP8 e4m3fn quantization, the front end of the FP8 path.
  *

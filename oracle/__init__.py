@@ -19,7 +19,8 @@ Modules:
 * ``attention`` -- exact causal softmax attention in fp64 (the plain
   definition that tiled online-softmax attention reproduces, [P1] "Why prefill
   attention deserves dedicated optimization"; the pages' own accuracy yardstick
-  is fp64 attention, [P3] "ZYFA 的 FP8 注意力有多准确？").
+  is fp64 attention, [P3] "ZYFA 的 FP8 注意力有多准确？"), also for a chunk of
+  queries after a key prefix, with the log-sum-exp of each row.
 * ``e4m3`` -- the OCP FP8 e4m3fn code: decode and round-to-nearest-even
   saturating encode ([P1] "ZYFA's performance and accuracy data" describes the
   format; [P3] "ZYFA 如何工作？" uses its integer ordering).
@@ -31,7 +32,7 @@ Every function is pinned by a ``-m "not gpu"`` test against something other than
 itself (library routines, closed forms, invariants, brute force).
 """
 
-from .attention import attn_ref, attn_ref_rows, causal_weights_ref  # noqa: F401
+from .attention import attn_chunk_ref_rows, attn_ref, attn_ref_rows, causal_weights_ref  # noqa: F401
 from .e4m3 import e4m3_decode, e4m3_encode_rne_sat  # noqa: F401
 from .hadamard import fwht128_f32, sylvester_hadamard  # noqa: F401
 from .quantize import quantize_ref, dequantize_ref  # noqa: F401

@@ -32,9 +32,9 @@ def lib():
     return pkg.load_library()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_five_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["attn_fwd", "attn_quantize_fp8", "attn_status_string", "attn_version"])
+        ["attn_fwd", "attn_fwd_chunk", "attn_quantize_fp8", "attn_status_string", "attn_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -47,14 +47,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert pkg.attn_version() == header_constant("MIATTN_ABI_VERSION")
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = pkg.attn_status_string(code)
         assert s and s != "unknown status code"
     assert pkg.attn_status_string(-99) == "unknown status code"
 
 
 OK = 0
-E_NULL, E_SIZE, E_SHAPE, E_DTYPE, E_HIP, E_ALIGN = -1, -2, -3, -4, -5, -6
+E_NULL, E_SIZE, E_SHAPE, E_DTYPE, E_HIP, E_ALIGN, E_VALUE = -1, -2, -3, -4, -5, -6, -7
 P = 1 << 20  # a 16-byte-aligned stand-in address; never dereferenced on these paths
 
 
@@ -74,6 +74,23 @@ def fwd(lib, q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, N=8, dqk=128, dv=128, dtype=0
 ])
 def test_attn_fwd_validation(lib, kw, expect):
     assert fwd(lib, **kw) == expect
+
+
+def chunk(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=128, dv=128, dtype=0, qs=P, ks=P,
+          vs=P, tau=0.0):
+    return lib.attn_fwd_chunk(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, dtype, qs, ks, vs, tau, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), E_NULL), (dict(o=None), E_NULL), (dict(dtype=1, ks=None), E_NULL),
+    (dict(Nq=21), E_SIZE), (dict(Nq=-1), E_SIZE), (dict(Nk=-3, Nq=0), E_SIZE), (dict(Hq=3, Hkv=2), E_SIZE),
+    (dict(dqk=64), E_SHAPE), (dict(dtype=3), E_DTYPE),
+    (dict(lse=P + 2), E_ALIGN), (dict(v=P + 4), E_ALIGN),
+    (dict(tau=-0.5), E_VALUE), (dict(tau=float("inf")), E_VALUE), (dict(tau=float("nan")), E_VALUE),
+    (dict(Nq=0), OK), (dict(B=0), OK), (dict(Nq=0, Nk=0), OK), (dict(Nq=0, q=None, k=None, v=None, o=None), OK),
+])
+def test_attn_fwd_chunk_validation(lib, kw, expect):
+    assert chunk(lib, **kw) == expect
 
 
 def quant(lib, x=P, src=0, y=P, s=P, B=1, H=2, N=8, d=128, had=0):
@@ -98,5 +115,7 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pkg.attn_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_chunk(q, q, q)
     with pytest.raises(ValueError):
         pkg.attn_quantize_fp8(q.float())
