@@ -21,7 +21,14 @@ peak of its dtype.  ``cpu_baseline`` times the CPU oracle (test
 infrastructure, untuned) on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-bf16] [--no-cpu-baseline]
+                       [--no-bf16] [--no-cpu-baseline] [--no-chunk]
+       python bench.py --clock-study [--study-seconds S]
+
+``--clock-study`` measures how the input data moves the sustained clock and
+the energy per FLOP: for several input distributions of the 32K workloads it
+runs back-to-back launches for a few seconds while sampling the graphics clock
+and reading the board's energy counter (amdsmi), and prints one JSON line per
+case (time, TFLOP/s, mean SCLK, mean power, TFLOP/J).
 """
 
 from __future__ import annotations
@@ -241,6 +248,98 @@ def cpu_baseline(w, budget_s: float = 12.0):
     }
 
 
+def clock_study(seconds: float):
+    """One JSON line per (dtype, input distribution): the data-dependent clock
+    and energy of the attention kernel on the 32K workloads."""
+    import threading
+
+    import torch
+
+    import bf16_causal_prefill_flashattention_amd as miattn
+    from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS, make_qkv
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # the readings are optional; timing still runs
+        print(f"amdsmi unavailable ({e}); clock and power are not reported", file=sys.stderr)
+        handle = None
+
+    def energy_j():
+        r = amdsmi.amdsmi_get_energy_count(handle)
+        return r["energy_accumulator"] * r["counter_resolution"] * 1e-6
+
+    dev = torch.device("cuda:0")
+    cases = [
+        ("gaussian", lambda q, k, v: (q, k, v)),
+        ("outlier_channels", None),  # 4 aligned channels x20 on Q and K
+        ("peaked_q_x4", lambda q, k, v: (q * 4, k, v)),  # near one-hot rows
+        ("flat_q_zero", lambda q, k, v: (torch.zeros_like(q), k, v)),  # all probabilities equal
+        ("zero_v", lambda q, k, v: (q, k, torch.zeros_like(v))),
+    ]
+    for wname in ("fp8_mha_n32k", "bf16_mha_n32k"):
+        base = WORKLOADS[wname]
+        for cname, fn in cases:
+            w = base.with_(outliers=4) if fn is None else base
+            q, k, v = make_qkv(w)
+            if fn is not None:
+                q, k, v = fn(q, k, v)
+            q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))
+            if w.dtype == "fp8":
+                (cq, sq), (ck, sk), (cv, sv) = (miattn.attn_quantize_fp8(t) for t in (q, k, v))
+                args = (cq, ck, cv, sq, sk, sv)
+            else:
+                args = (q, k, v)
+            out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+            for _ in range(20):
+                miattn.attn_fwd(*args, out=out)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            miattn.attn_fwd(*args, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
+            clocks, stop = [], threading.Event()
+
+            def sample():
+                while not stop.wait(0.05):
+                    try:
+                        clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+                    except Exception:
+                        pass
+
+            th = None
+            if handle is not None:
+                th = threading.Thread(target=sample, daemon=True)
+                ej0, t0 = energy_j(), time.perf_counter()
+                th.start()
+            e0.record()
+            for _ in range(n):
+                miattn.attn_fwd(*args, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            rec = {"study": "clock_energy", "workload": wname, "inputs": cname, "launches": n,
+                   "ms_per_launch": round(ms, 4), "tflops": round(w.causal_flops / (ms * 1e-3) / 1e12, 1)}
+            if th is not None:
+                t1, ej1 = time.perf_counter(), energy_j()
+                stop.set()
+                th.join()
+                watts = (ej1 - ej0) / (t1 - t0)
+                rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
+                rec["sclk_samples"] = len(clocks)
+                rec["board_watts_mean"] = round(watts, 1)
+                rec["tflop_per_joule"] = round(rec["tflops"] / watts, 3) if watts > 0 else None
+            print(json.dumps(rec), flush=True)
+            del args, out, q, k, v
+            torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +350,8 @@ def main(argv=None):
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--clock-study", action="store_true")
+    ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -269,6 +370,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.clock_study:
+        return clock_study(args.study_seconds)
     w = WORKLOADS[args.workload]
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
