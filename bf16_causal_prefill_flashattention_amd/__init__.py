@@ -13,6 +13,9 @@ Entry points (same names as the C ABI):
   lse=None, with_lse=True, softmax_scale=None)``
 * ``attn_quantize_fp8(x, hadamard=False, out=None, scale=None)``
 * ``attn_status_string(status)``, ``attn_version()``
+
+and ``flash_attn_func``, a ``flash_attn_func``-style drop-in over them (BSHD
+torch tensors in, causal, optional FP8 with automatic per-head quantization).
 """
 
 from __future__ import annotations
@@ -26,6 +29,7 @@ __all__ = [
     "attn_quantize_fp8",
     "attn_status_string",
     "attn_version",
+    "flash_attn_func",
     "library_path",
     "load_library",
     "MiattnError",
@@ -236,3 +240,36 @@ def attn_quantize_fp8(x, hadamard: bool = False, out=None, scale=None):
     if st != 0:
         raise MiattnError("attn_quantize_fp8", st)
     return out, scale
+
+
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, return_lse=False, fp8=False,
+                    hadamard=False):
+    """Drop-in for the ``flash_attn_func`` call convention: q [B,Nq,Hq,d_qk],
+    k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] BF16 GPU tensors (BSHD), causal, with
+    Nq <= Nk (the queries are the last Nq positions; Nq == Nk is a plain
+    prefill).  ``fp8=True`` quantizes q, k, v per (batch, head) to e4m3 with
+    the library's quantizer (``hadamard=True`` rotates q and k first, d = 128)
+    and runs the FP8 path.  Returns the bf16 output, or ``(out, lse)`` with
+    ``return_lse`` (lse fp32 [B,Hq,Nq], natural log).  Only what the kernels
+    compute is accepted: causal=False and dropout raise."""
+    torch = _torch()
+    if not causal:
+        raise NotImplementedError("only causal attention is implemented")
+    if dropout_p:
+        raise NotImplementedError("dropout is not implemented (forward inference only)")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16 (fp8=True quantizes it)")
+    if hadamard and not fp8:
+        raise ValueError("hadamard applies to the FP8 path only")
+    if fp8:
+        (cq, sq) = attn_quantize_fp8(q.contiguous(), hadamard=hadamard)
+        (ck, sk) = attn_quantize_fp8(k.contiguous(), hadamard=hadamard)
+        (cv, sv) = attn_quantize_fp8(v.contiguous())
+        args = (cq, ck, cv, sq, sk, sv)
+    else:
+        args = (q.contiguous(), k.contiguous(), v.contiguous())
+    if q.shape[1] == k.shape[1] and softmax_scale is None and not return_lse:
+        return attn_fwd(*args)
+    out, lse = attn_fwd_chunk(*args, with_lse=return_lse, softmax_scale=softmax_scale)
+    return (out, lse) if return_lse else out

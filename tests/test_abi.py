@@ -119,3 +119,19 @@ def test_binding_refuses_cpu_tensors():
         pkg.attn_fwd_chunk(q, q, q)
     with pytest.raises(ValueError):
         pkg.attn_quantize_fp8(q.float())
+
+
+def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
+    import torch
+
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(NotImplementedError):
+        pkg.flash_attn_func(q, q, q, causal=False)
+    with pytest.raises(NotImplementedError):
+        pkg.flash_attn_func(q, q, q, dropout_p=0.1)
+    with pytest.raises(TypeError):
+        pkg.flash_attn_func(q.float(), q.float(), q.float())
+    with pytest.raises(ValueError):
+        pkg.flash_attn_func(q, q, q, hadamard=True)
+    with pytest.raises(ValueError):  # CPU tensors
+        pkg.flash_attn_func(q, q, q)

@@ -233,3 +233,28 @@ def test_full_size_chunk_sampled_rows(require_gpu):
         ref_in = (dequantize_ref(rq, rsq), dequantize_ref(rk, rsk), None)
         _check_lse("fp8", lse[:, h:h + 1, rows], ref_lse, ref_in, rows=rows)
     assert max(errs) <= TOL["fp8"], errs
+
+
+@pytest.mark.parametrize("fp8,hadamard,Nq,Nk,tau,ret", [
+    (False, False, 500, 500, None, False), (False, False, 300, 900, 0.1, True),
+    (True, False, 700, 700, None, False), (True, True, 256, 1024, None, True), (True, False, 64, 2000, 0.05, True),
+])
+def test_flash_attn_func_drop_in(require_gpu, fp8, hadamard, Nq, Nk, tau, ret):
+    """BF16 tensors in; with fp8=True the library quantizes (and rotates) them.
+    The oracle runs on the inputs the kernel consumed: the BF16 values, or the
+    oracle quantizer's codes (which the GPU quantizer matches bit for bit)."""
+    q, k, v = (t.to(torch.bfloat16) for t in _case("bf16", 1, Nq, Nk, 4, 2, 128, seed=Nq + Nk))
+    res = miattn.flash_attn_func(q.cuda(), k.cuda(), v.cuda(), softmax_scale=tau, return_lse=ret, fp8=fp8,
+                                 hadamard=hadamard)
+    torch.cuda.synchronize()
+    out, lse = res if ret else (res, None)
+    if fp8:
+        (cq, sq), (ck, sk), (cv, sv) = quantize_ref(q, hadamard), quantize_ref(k, hadamard), quantize_ref(v, False)
+        ref_in = (dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
+    else:
+        ref_in = (q, k, v)
+    ref, ref_lse = attn_chunk_ref_rows(*ref_in, softmax_scale=tau)
+    dtype = "fp8" if fp8 else "bf16"
+    assert rel_fro(out.cpu(), ref) <= TOL[dtype]
+    if ret:
+        _check_lse(dtype, lse.cpu().numpy().astype(np.float64), ref_lse, ref_in, softmax_scale=tau)
