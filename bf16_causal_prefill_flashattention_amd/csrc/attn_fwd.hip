@@ -46,7 +46,8 @@
 // XOR swizzle of their 16-byte chunks so that the rows one operand read
 // touches fall in distinct LDS banks; the V^T operand is read with the
 // transposing LDS reads of gfx950.  Two LDS buffers each for K and V; the loads
-// of phase 2p are waited for at the end of phase 2p+1.  Rows at or beyond Nq
+// of step p (issued in phase 2p, or early in phase 2p+1) are waited for at the
+// end of phase 2p+1.  Rows at or beyond Nq
 // (queries) or Nk (keys), and whole tiles past the last one a workgroup needs,
 // load as zeros (buffer bounds), so ragged tiles and the loads of the final
 // steps need no branches; keys >= Nk lie above the diagonal of every valid
@@ -639,19 +640,20 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   // ---- main loop: steps 0..T (step T only drains P_{T-1} V_{T-1})
   // Both groups run the same matrix/vector code; only where each issues its
   // share of the tile loads and which barrier waits for them differ:
-  //   group A: loads(p), matrix(p) | barrier | vector(p), wait | barrier
+  //   group A: matrix(p) | barrier | vector(p), wait | barrier
   //   group B: matrix(p), wait | barrier | vector(p), loads(p+1) | barrier
-  // Group A's loads go at the start of its matrix phase for FP8 and at its end
-  // for BF16, group B's at the end of its vector phase: the positions measured
-  // fastest for each (the loads of one phase are waited for at the end of the
-  // next, when every wave has issued its share).
-  constexpr bool A_LOADS_LATE = !FP8;
+  // Group A issues its loads of step p before its matrix work for FP8 and at
+  // the start of its vector work for BF16: the FP8 softmax is the longer half
+  // of a phase and the BF16 matrix work is (the loads take the CU's load path
+  // for a few hundred cycles, so they go where the wave has slack).  Group B
+  // issues at the end of its vector work.  Every load of step p is waited for
+  // at the barrier that ends phase 2p+1, when all waves have issued theirs.
   auto step = [&](int ps, auto parity, auto group) __attribute__((always_inline)) {
     constexpr bool GA = decltype(group)::value == 0;
-    if (GA && !A_LOADS_LATE) issue_step(ps);
+    if (GA && FP8) issue_step(ps);
     matrix_work(ps, parity);
-    if (GA && A_LOADS_LATE) issue_step(ps);
     barrier(!GA);
+    if (GA && !FP8) issue_step(ps);
     vector_work(ps);
     if (!GA) issue_step(ps + 1);
     barrier(GA);
