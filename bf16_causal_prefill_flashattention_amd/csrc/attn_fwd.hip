@@ -290,10 +290,13 @@ struct Wave {
 }  // namespace
 
 // One work item: the kBM queries of query tile qt of (batch, head) bh, against
-// all keys up to the last of them.  Called by every thread of the workgroup;
-// leaves no load in flight and no wave reading LDS when it returns.
+// all keys up to the last of them.  Key tiles are visited in increasing order,
+// or from the last one down when `rev` is set (the softmax is the same in any
+// key order; the order only decides which tiles the workgroups of an XCD read
+// at the same time).  Called by every thread of the workgroup; leaves no load
+// in flight and no wave reading LDS when it returns.
 template <int DQK, int DV, bool FP8>
-__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, int bh, int qt) {
+__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, int bh, int qt, bool rev) {
   using C = Cfg<FP8, DQK, DV>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
@@ -376,6 +379,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   const int T = (kend + BN - 1) / BN;        // key tiles of the workgroup
   // tiles this wave needs: keys up to the position of its last valid query
   const int Tw = qw0 < Nq ? ((min(qw0 + 31, Nq - 1) + off) / BN + 1) : 0;
+  // steps [s_lo, s_hi) carry the wave's tiles; step s visits tile tile_of(s),
+  // and steps at or beyond T map to tile T (an empty load range)
+  const int s_lo = rev ? T - Tw : 0, s_hi = rev ? T : Tw;
+  const int t_base = rev ? T - 1 : 0, t_dir = rev ? -1 : 1;
+  // (unsigned min: the -1 of a downward walk past tile 0 also maps to T)
+  auto tile_of = [&](int s) __attribute__((always_inline)) {
+    return (int)min((uint32_t)(t_base + t_dir * s), (uint32_t)T);
+  };
 
   // tiles at or beyond T load with an empty range (zeros, no memory access), so
   // the loads need no branches
@@ -401,8 +412,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   };
   // loads of step p: K tile p+1 and V tile p
   auto issue_step = [&](int pstep) __attribute__((always_inline)) {
-    issue_k(pstep + 1, (pstep + 1) & 1);
-    issue_v(pstep, pstep & 1);
+    issue_k(tile_of(pstep + 1), (pstep + 1) & 1);
+    issue_v(tile_of(pstep), pstep & 1);
   };
 
   // ---- Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16),
@@ -537,17 +548,18 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
     const uint8_t* vb = Vs + (1 - PAR) * C::V_TILE;       // V tile pstep-1
     const uint8_t* kb = Ks + PAR * C::K_TILE;  // K tile pstep
     // One instruction sequence for every step the wave takes part in (a single
-    // variant keeps the register allocation tight): at step 0 the P.V product
-    // multiplies zero probabilities with a zero-filled V buffer, and at step Tw
-    // the scores of a tile the wave does not need are computed and never read.
-    if (pstep <= Tw)
+    // variant keeps the register allocation tight): at step s_lo the P.V
+    // product multiplies the zero probabilities the item starts with (by a
+    // zero-filled or fully loaded V buffer), and at step s_hi the scores of a
+    // tile the wave does not need are computed and never read.
+    if (pstep >= s_lo && pstep <= s_hi)
       run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
   };
 
   // ---- vector work of step pstep: online softmax of S_pstep -> probabilities.
   auto vector_work = [&](int pstep) __attribute__((always_inline)) {
-    if (pstep < 0 || pstep >= Tw) return;
-    const int kb = pstep * BN;
+    if (pstep < s_lo || pstep >= s_hi) return;
+    const int kb = tile_of(pstep) * BN;
     if (kb + BN - 1 > qw0 + off) {  // the tile crosses this wave's diagonal: mask keys above each query
       // key offset k of register r is visible iff k <= lim; the sign of lim - k
       // selects -inf bit by bit (no per-element compare masks held in SGPRs)
@@ -625,7 +637,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 
   // ---- prologue: K tile 0 into buffer 0; V buffer 1 (read by the empty P.V
   // product of step 0) and the probabilities start at zero.
-  issue_k(0, 0);
+  issue_k(tile_of(0), 0);
 #pragma unroll
   for (int i = 0; i < C::V_TILE / (16 * kThreads); ++i)
     lds_store16(Vs + C::V_TILE + 16 * (tid + kThreads * i), i32x4{0, 0, 0, 0});
@@ -701,7 +713,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 // only serialize short work).  Workgroup w runs on XCD w % 8 (round-robin
 // dispatch); when the (batch, head) count splits evenly over the 8 XCDs, XCD x
 // takes the heads bh = x (mod 8) and its workgroups sweep one head at a time,
-// so the K/V tiles they stream are shared in that XCD's L2.
+// so the K/V tiles they stream are shared in that XCD's L2.  The heavier tile of
+// a unit walks its keys upward and the lighter one downward: with units of
+// equal cost started together, every workgroup of an XCD then reads key tile t
+// at about the same moment in both halves (time t in the heavy half, a constant
+// minus t in the light half), so the workgroups stream two shared fronts of K/V
+// tiles instead of one stream each.
 template <int DQK, int DV, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
@@ -721,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
     const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
     const int j = u % per_bh;
     const int qt = half == 0 ? nqt - 1 - j : j;
-    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8>(p, smem, bh, qt);
+    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8>(p, smem, bh, qt, !single && half == 1);
     if (single) {
       u += nrank;
     } else {
