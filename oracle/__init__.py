@@ -24,9 +24,12 @@ Modules:
 * ``e4m3`` -- the OCP FP8 e4m3fn code: decode and round-to-nearest-even
   saturating encode ([P1] "ZYFA's performance and accuracy data" describes the
   format; [P3] "ZYFA 如何工作？" uses its integer ordering).
-* ``hadamard`` -- the 128-point Sylvester Hadamard rotation of Q and K
-  ([P3] "ZYFA 的 FP8 注意力有多准确？", [P2] "Accuracy and Code").
-* ``quantize`` -- per-(batch, head) amax/448 FP8 quantization.
+* ``hadamard`` -- the Sylvester Hadamard rotation of Q and K along the head
+  dimension (one H_128 at d = 128, three H_64 blocks at d = 192) ([P3] "ZYFA 的
+  FP8 注意力有多准确？", [P2] "Accuracy and Code").
+* ``quantize`` -- per-(batch, head) amax/448 FP8 quantization, and per-64-position
+  block quantization with power-of-two scales ([P1] "ZYFA's performance and
+  accuracy data" names scaling granularity).
 
 Every function is pinned by a ``-m "not gpu"`` test against something other than
 itself (library routines, closed forms, invariants, brute force).
@@ -34,5 +37,17 @@ itself (library routines, closed forms, invariants, brute force).
 
 from .attention import attn_chunk_ref_rows, attn_ref, attn_ref_rows, causal_weights_ref  # noqa: F401
 from .e4m3 import e4m3_decode, e4m3_encode_rne_sat  # noqa: F401
-from .hadamard import fwht128_f32, sylvester_hadamard  # noqa: F401
-from .quantize import quantize_ref, dequantize_ref  # noqa: F401
+from .hadamard import (  # noqa: F401
+    fwht128_f32,
+    fwht_f32,
+    hadamard_norm_f32,
+    hadamard_rotate_f32,
+    sylvester_hadamard,
+)
+from .quantize import (  # noqa: F401
+    block_exponent,
+    dequantize_block64_ref,
+    dequantize_ref,
+    quantize_block64_ref,
+    quantize_ref,
+)

@@ -99,3 +99,31 @@ def test_quantize_mutant_is_caught():
     x = np.random.default_rng(3).standard_normal((1, 50, 1, 128)).astype(np.float32)
     codes, _ = m.quantize_ref(x)
     assert not np.any((codes & 0x7F) == 0x7E)  # the amax element no longer maps to 448
+
+
+BLOCK64_MUTANTS = [
+    ("y = (xs * np.float32(math.ldexp(1.0, -e)))", "y = (xs * np.float32(math.ldexp(1.0, e)))"),  # inverse scale
+    ("math.frexp(float(amax))[1] - 9", "math.frexp(float(amax))[1] - 8"),  # exponent one too large
+    ("* hadamard_norm_f32(d)).astype", ").astype"),  # normalisation dropped
+    ("scales[b, h, j] = np.float32(math.ldexp(1.0, e))", "scales[b, h, j] = np.float32(math.ldexp(1.0, e - 1))"),
+]
+
+
+@pytest.mark.parametrize("old,new", BLOCK64_MUTANTS)
+def test_block64_mutants_are_caught(old, new):
+    from oracle.hadamard import hadamard_rotate_f32
+
+    m = _load_mutant("quantize.py", old, new)
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((1, 130, 1, 128)) * 10.0 ** g.uniform(-2, 2)).astype(np.float32)
+    x[0, :64] *= np.float32(3.7)
+    ok = True
+    for had in (False, True):
+        codes, scales = m.quantize_block64_ref(x, had)
+        ref = hadamard_rotate_f32(x).astype(np.float64) * 2.0 ** -3.5 if had else x.astype(np.float64)
+        deq = m.dequantize_block64_ref(codes, scales)
+        ok &= bool(np.linalg.norm(deq - ref) / np.linalg.norm(ref) < 0.04)
+        for j in range(3):
+            amax = np.abs(ref[0, 64 * j:64 * (j + 1)]).max()
+            ok &= bool(224 < amax / float(scales[0, 0, j]) <= 448 * (1 + 1e-6))
+    assert not ok
