@@ -12,7 +12,9 @@ on its own under ``front_end``.  The BF16 point of the same metric (BF16,
 d = 128, N = 32K) is reported in the same line under ``bf16``, and one chunk
 of a chunked prefill (the last 8192 positions of the same 32K FP8 sequence
 against all 32768 keys, with the LSE output) under ``chunk``, its FLOPs
-counted the same way: B * Hq * (2 Nq Nk - Nq^2) * (d_qk + d_v).
+counted the same way: B * Hq * (2 Nq Nk - Nq^2) * (d_qk + d_v).  The same FP8
+workload quantized with one power-of-two scale per 64 positions instead of
+one per head (``attn_fwd_block64``) is reported under ``block64``.
 
 ``roofline`` describes the attention kernel (the dominant one): its algorithmic
 FLOPs per launch divided by its average launch duration, measured with HIP
@@ -21,7 +23,7 @@ peak of its dtype.  ``cpu_baseline`` times the CPU oracle (test
 infrastructure, untuned) on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-bf16] [--no-cpu-baseline] [--no-chunk]
+                       [--no-bf16] [--no-cpu-baseline] [--no-chunk] [--no-block64]
        python bench.py --clock-study [--study-seconds S]
 
 ``--clock-study`` measures how the input data moves the sustained clock and
@@ -84,6 +86,7 @@ def run_gpu(w, steps: int, warmup: int):
     q, k, v = make_qkv(w)
     q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))  # BF16 activations in HBM
     fp8 = w.dtype == "fp8"
+    block64 = fp8 and w.scales == "block64"
     out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)  # every kernel below is enqueued on this stream
     front_ms = None
@@ -91,14 +94,16 @@ def run_gpu(w, steps: int, warmup: int):
         cq = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         ck = torch.empty(k.shape, dtype=torch.uint8, device=dev)
         cv = torch.empty(v.shape, dtype=torch.uint8, device=dev)
-        sq = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
-        sk = torch.empty((w.B, w.Hkv), dtype=torch.float32, device=dev)
-        sv = torch.empty((w.B, w.Hkv), dtype=torch.float32, device=dev)
+        nb = ((w.N + 63) // 64,) if block64 else ()
+        sq = torch.empty((w.B, w.Hq) + nb, dtype=torch.float32, device=dev)
+        sk = torch.empty((w.B, w.Hkv) + nb, dtype=torch.float32, device=dev)
+        sv = torch.empty((w.B, w.Hkv) + nb, dtype=torch.float32, device=dev)
+        quantize = miattn.attn_quantize_fp8_block64 if block64 else miattn.attn_quantize_fp8
 
         def front_end():
-            miattn.attn_quantize_fp8(q, hadamard=w.hadamard, out=cq, scale=sq)
-            miattn.attn_quantize_fp8(k, hadamard=w.hadamard, out=ck, scale=sk)
-            miattn.attn_quantize_fp8(v, hadamard=False, out=cv, scale=sv)
+            quantize(q, hadamard=w.hadamard, out=cq, scale=sq)
+            quantize(k, hadamard=w.hadamard, out=ck, scale=sk)
+            quantize(v, hadamard=False, out=cv, scale=sv)
 
         # the FP8 front end, timed on its own (it also leaves the resident inputs)
         fe = []
@@ -118,7 +123,10 @@ def run_gpu(w, steps: int, warmup: int):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        miattn.attn_fwd(*args, out=out)
+        if block64:
+            miattn.attn_fwd_block64(*args, out=out, with_lse=False)
+        else:
+            miattn.attn_fwd(*args, out=out)
         if ev is not None:
             ev[1].record(stream)
 
@@ -188,7 +196,7 @@ def roofline(w, attn_ms, flops=None):
     achieved = flops / avg_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     return {
-        "kernel": f"attn_fwd_{w.dtype}_kernel<{w.d_qk},{w.d_v}>",
+        "kernel": f"attn_fwd_{w.dtype}{'_block64' if w.scales == 'block64' else ''}_kernel<{w.d_qk},{w.d_v}>",
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": peak,
@@ -350,6 +358,7 @@ def main(argv=None):
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-block64", action="store_true")
     ap.add_argument("--clock-study", action="store_true")
     ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
@@ -414,6 +423,18 @@ def main(argv=None):
             "ms_per_step": round(msb, 4),
             "roofline": roofline(wb, attn_b),
         }
+    if not args.no_block64 and w.name == "fp8_mha_n32k":
+        wq = WORKLOADS["fp8_mha_n32k_block64"]
+        msq, attn_q, front_q = run_gpu(wq, args.steps, args.warmup)
+        rec["block64"] = {
+            "workload": f"{wq.name}: the same inputs with one power-of-two scale per 64 positions "
+                        "(K and V scales applied by the scaled MFMAs)",
+            "value": round(wq.causal_flops / (msq * 1e-3) / 1e12, 1),
+            "ms_per_step": round(msq, 4),
+            "front_end_ms": round(front_q, 4),
+            "roofline": roofline(wq, attn_q),
+        }
+        rec["block64"]["roofline"]["traffic"] = None
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
         msc, attn_c = run_chunk(w, Nq, args.steps, args.warmup)

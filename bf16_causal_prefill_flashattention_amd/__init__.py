@@ -12,10 +12,14 @@ Entry points (same names as the C ABI):
 * ``attn_fwd_chunk(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None,
   lse=None, with_lse=True, softmax_scale=None)``
 * ``attn_quantize_fp8(x, hadamard=False, out=None, scale=None)``
+* ``attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None,
+  with_lse=True, softmax_scale=None)`` (FP8 with per-64-position scales)
+* ``attn_quantize_fp8_block64(x, hadamard=False, out=None, scale=None)``
 * ``attn_status_string(status)``, ``attn_version()``
 
 and ``flash_attn_func``, a ``flash_attn_func``-style drop-in over them (BSHD
-torch tensors in, causal, optional FP8 with automatic per-head quantization).
+torch tensors in, causal, optional FP8 with automatic per-head or
+per-64-position quantization).
 """
 
 from __future__ import annotations
@@ -25,8 +29,10 @@ import os
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_block64",
     "attn_fwd_chunk",
     "attn_quantize_fp8",
+    "attn_quantize_fp8_block64",
     "attn_status_string",
     "attn_version",
     "flash_attn_func",
@@ -75,6 +81,10 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_chunk.restype = ci
     lib.attn_quantize_fp8.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8.restype = ci
+    lib.attn_fwd_block64.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, vp]
+    lib.attn_fwd_block64.restype = ci
+    lib.attn_quantize_fp8_block64.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
+    lib.attn_quantize_fp8_block64.restype = ci
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -118,9 +128,10 @@ def _as_codes(name, t):
     raise TypeError(f"{name} must be uint8 or float8_e4m3fn codes for the FP8 path")
 
 
-def _attn_args(q, k, v, q_scale, k_scale, v_scale):
+def _attn_args(q, k, v, q_scale, k_scale, v_scale, block64=False):
     """Check q [B,Nq,Hq,d_qk], k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] and the FP8
-    scales; returns (q, k, v, dtype code, scale pointers, sizes)."""
+    scales (per head, or per 64 positions with ``block64``); returns (q, k, v,
+    dtype code, scale pointers, sizes)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu_contig(name, t)
@@ -130,7 +141,7 @@ def _attn_args(q, k, v, q_scale, k_scale, v_scale):
     Nk, Hkv, dv = k.shape[1], k.shape[2], v.shape[3]
     if tuple(k.shape) != (B, Nk, Hkv, dqk) or tuple(v.shape[:3]) != (B, Nk, Hkv):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
-    if q.dtype == torch.bfloat16:
+    if q.dtype == torch.bfloat16 and not block64:
         if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
             raise TypeError("q, k, v must share one dtype")
         dtype = DTYPE_BF16
@@ -139,8 +150,9 @@ def _attn_args(q, k, v, q_scale, k_scale, v_scale):
         q, k, v = _as_codes("q", q), _as_codes("k", k), _as_codes("v", v)
         dtype = DTYPE_FP8_E4M3
         scales = []
-        for name, s, shape in (("q_scale", q_scale, (B, Hq)), ("k_scale", k_scale, (B, Hkv)),
-                               ("v_scale", v_scale, (B, Hkv))):
+        nbq, nbk = (Nq + 63) // 64, (Nk + 63) // 64
+        shapes = ((B, Hq, nbq), (B, Hkv, nbk), (B, Hkv, nbk)) if block64 else ((B, Hq), (B, Hkv), (B, Hkv))
+        for name, s, shape in zip(("q_scale", "k_scale", "v_scale"), (q_scale, k_scale, v_scale), shapes):
             if s is None:
                 raise ValueError(f"{name} is required for the FP8 path")
             _check_gpu_contig(name, s)
@@ -190,15 +202,9 @@ def attn_fwd_chunk(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None, 
     out bf16 [B,Nq,Hq,d_v]; lse fp32 [B,Hq,Nq], the natural-log sum of
     exp(tau <q_i, k_j>) over the visible keys, or None when ``with_lse`` is
     false and no ``lse`` tensor is given."""
-    torch = _torch()
     q, k, v, dtype, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale)
     out = _out_tensor(out, q, B, Nq, Hq, dv)
-    if lse is None and with_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_gpu_contig("lse", lse)
-        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
-            raise ValueError(f"lse must be float32 {(B, Hq, Nq)}")
+    lse = _lse_tensor(lse, with_lse, q, B, Hq, Nq)
     st = load_library().attn_fwd_chunk(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
         B, Hq, Hkv, Nq, Nk, dqk, dv, dtype, ptr_s[0], ptr_s[1], ptr_s[2],
@@ -212,6 +218,44 @@ def attn_fwd_chunk(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None, 
 def attn_quantize_fp8(x, hadamard: bool = False, out=None, scale=None):
     """Per-(batch, head) FP8 e4m3fn quantization of x [B,N,H,d] (fp32 or bf16,
     on a GPU).  Returns (codes uint8 [B,N,H,d], scale fp32 [B,H])."""
+    return _quantize("attn_quantize_fp8", x, hadamard, out, scale, lambda B, N, H: (B, H))
+
+
+def _lse_tensor(lse, with_lse, q, B, Hq, Nq):
+    torch = _torch()
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_gpu_contig("lse", lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError(f"lse must be float32 {(B, Hq, Nq)}")
+    return lse
+
+
+def attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, with_lse=True, softmax_scale=None):
+    """FP8 causal attention with per-64-position scales: q [B,Nq,Hq,d_qk],
+    k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] e4m3 codes (uint8 or float8_e4m3fn),
+    q_scale fp32 [B,Hq,ceil(Nq/64)], k_scale and v_scale fp32
+    [B,Hkv,ceil(Nk/64)] (powers of two, as ``attn_quantize_fp8_block64``
+    writes them).  Query row i sees keys j <= i + Nk - Nq.  Returns
+    ``(out, lse)`` as ``attn_fwd_chunk``."""
+    torch = _torch()
+    if q.dtype == torch.bfloat16:
+        raise TypeError("attn_fwd_block64 takes e4m3 codes (quantize with attn_quantize_fp8_block64)")
+    q, k, v, _, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale, True)
+    out = _out_tensor(out, q, B, Nq, Hq, dv)
+    lse = _lse_tensor(lse, with_lse, q, B, Hq, Nq)
+    st = load_library().attn_fwd_block64(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, dqk, dv, ptr_s[0], ptr_s[1], ptr_s[2],
+        0.0 if softmax_scale is None else float(softmax_scale), _stream_handle(q.device),
+    )
+    if st != 0:
+        raise MiattnError("attn_fwd_block64", st)
+    return out, lse
+
+
+def _quantize(fn_name, x, hadamard, out, scale, scale_shape):
     torch = _torch()
     _check_gpu_contig("x", x)
     if x.dim() != 4:
@@ -223,35 +267,45 @@ def attn_quantize_fp8(x, hadamard: bool = False, out=None, scale=None):
     else:
         raise TypeError("x must be float32 or bfloat16")
     B, N, H, d = x.shape
+    shape = scale_shape(B, N, H)
     if out is None:
         out = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
     if scale is None:
-        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+        scale = torch.empty(shape, dtype=torch.float32, device=x.device)
     _check_gpu_contig("out", out)
     _check_gpu_contig("scale", scale)
     if out.dtype != torch.uint8 or tuple(out.shape) != (B, N, H, d):
         raise ValueError("out must be uint8 [B, N, H, d]")
-    if scale.dtype != torch.float32 or tuple(scale.shape) != (B, H):
-        raise ValueError("scale must be float32 [B, H]")
-    st = load_library().attn_quantize_fp8(
+    if scale.dtype != torch.float32 or tuple(scale.shape) != shape:
+        raise ValueError(f"scale must be float32 {shape}")
+    st = getattr(load_library(), fn_name)(
         x.data_ptr(), src, out.data_ptr(), scale.data_ptr(), B, H, N, d, 1 if hadamard else 0,
         _stream_handle(x.device),
     )
     if st != 0:
-        raise MiattnError("attn_quantize_fp8", st)
+        raise MiattnError(fn_name, st)
     return out, scale
 
 
+def attn_quantize_fp8_block64(x, hadamard: bool = False, out=None, scale=None):
+    """Per-64-position FP8 e4m3fn quantization of x [B,N,H,d] (fp32 or bf16,
+    on a GPU) with power-of-two scales.  Returns (codes uint8 [B,N,H,d],
+    scale fp32 [B,H,ceil(N/64)])."""
+    return _quantize("attn_quantize_fp8_block64", x, hadamard, out, scale, lambda B, N, H: (B, H, (N + 63) // 64))
+
+
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, return_lse=False, fp8=False,
-                    hadamard=False):
+                    hadamard=False, fp8_scales="head"):
     """Drop-in for the ``flash_attn_func`` call convention: q [B,Nq,Hq,d_qk],
     k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] BF16 GPU tensors (BSHD), causal, with
     Nq <= Nk (the queries are the last Nq positions; Nq == Nk is a plain
-    prefill).  ``fp8=True`` quantizes q, k, v per (batch, head) to e4m3 with
-    the library's quantizer (``hadamard=True`` rotates q and k first, d = 128)
-    and runs the FP8 path.  Returns the bf16 output, or ``(out, lse)`` with
-    ``return_lse`` (lse fp32 [B,Hq,Nq], natural log).  Only what the kernels
-    compute is accepted: causal=False and dropout raise."""
+    prefill).  ``fp8=True`` quantizes q, k, v to e4m3 with the library's
+    quantizer -- one scale per (batch, head) (``fp8_scales="head"``) or one
+    power-of-two scale per 64 positions (``fp8_scales="block64"``);
+    ``hadamard=True`` rotates q and k first -- and runs the FP8 path.  Returns
+    the bf16 output, or ``(out, lse)`` with ``return_lse`` (lse fp32
+    [B,Hq,Nq], natural log).  Only what the kernels compute is accepted:
+    causal=False and dropout raise."""
     torch = _torch()
     if not causal:
         raise NotImplementedError("only causal attention is implemented")
@@ -262,6 +316,14 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, ret
             raise TypeError(f"{name} must be bfloat16 (fp8=True quantizes it)")
     if hadamard and not fp8:
         raise ValueError("hadamard applies to the FP8 path only")
+    if fp8_scales not in ("head", "block64"):
+        raise ValueError('fp8_scales must be "head" or "block64"')
+    if fp8 and fp8_scales == "block64":
+        (cq, sq) = attn_quantize_fp8_block64(q.contiguous(), hadamard=hadamard)
+        (ck, sk) = attn_quantize_fp8_block64(k.contiguous(), hadamard=hadamard)
+        (cv, sv) = attn_quantize_fp8_block64(v.contiguous())
+        out, lse = attn_fwd_block64(cq, ck, cv, sq, sk, sv, with_lse=return_lse, softmax_scale=softmax_scale)
+        return (out, lse) if return_lse else out
     if fp8:
         (cq, sq) = attn_quantize_fp8(q.contiguous(), hadamard=hadamard)
         (ck, sk) = attn_quantize_fp8(k.contiguous(), hadamard=hadamard)

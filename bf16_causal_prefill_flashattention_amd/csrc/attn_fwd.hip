@@ -53,6 +53,14 @@
 // steps need no branches; keys >= Nk lie above the diagonal of every valid
 // query and are masked.
 //
+// FP8 scale granularity.  Either one fp32 scale per (batch, head) for each of
+// Q, K, V, folded into the score multiplier and the output, or one scale per
+// 64 positions: Q's per-wave block scale (a wave's 32 queries lie in one block)
+// goes into the score multiplier, and the power-of-two K and V block scales are
+// applied by the scaled MFMAs as E8M0 exponents (a 32-key QK block and a 64-key
+// P.V k-step each lie in one 64-key block), at no vector cost.  The exponents of
+// a work item's key tiles are staged in LDS, one word per 128-key tile.
+//
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
 // accumulator.  The row sum is taken from the rounded probabilities that feed
@@ -295,8 +303,9 @@ struct Wave {
 // key order; the order only decides which tiles the workgroups of an XCD read
 // at the same time).  Called by every thread of the workgroup; leaves no load
 // in flight and no wave reading LDS when it returns.
-template <int DQK, int DV, bool FP8>
-__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, int bh, int qt, bool rev) {
+template <int DQK, int DV, bool FP8, bool BS>
+__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
+                                          bool rev) {
   using C = Cfg<FP8, DQK, DV>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
@@ -326,7 +335,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 
   float c = p.sm_scale_log2;  // log2-domain score scale (dequantisation folded in for FP8)
   float sv = 1.f;
-  if constexpr (FP8) {
+  if constexpr (FP8 && BS) {
+    const int nbq = (Nq + 63) / 64;
+    c *= p.q_scale[((size_t)b * p.Hq + h) * nbq + min(qw0, Nq - 1) / 64];
+  } else if constexpr (FP8) {
     c *= p.q_scale[b * p.Hq + h] * p.k_scale[b * p.Hkv + g];
     sv = p.v_scale[b * p.Hkv + g];
   }
@@ -451,6 +463,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
   const int sel_w = sel_on ? (FP8 ? 0x38383838 : 0x3f803f80) : 0;  // e4m3 / bf16 ones
   const i32x8 sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
 
+  // E8M0 exponents of the K tile (bytes 0, 1: its two 64-key blocks) and V tile
+  // (bytes 2, 3) of the current matrix phase (block scales only)
+  uint32_t kexp = 0, vexp = 0;
+
   // ---- matrix work of step pstep: P_{pstep-1} V_{pstep-1}, then S_pstep = K_pstep Q^T.
   // The products form one list of MFMAs (PV first, then QK with the k-steps
   // outermost so consecutive MFMAs are independent); the LDS operand of MFMA
@@ -500,7 +516,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
                           (int)wv.pk[8 * ks + 3], (int)wv.pk[8 * ks + 4], (int)wv.pk[8 * ks + 5],
                           (int)wv.pk[8 * ks + 6], (int)wv.pk[8 * ks + 7]};
         if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
-        wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
+        if constexpr (BS)
+          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
+                                : mfma_fp8_32x32x64_sa<3>(a, pb, wv.st.o[db], (int)vexp);
+        else
+          wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
       } else {
         const int chunk = i / (DV / 32), db = i % (DV / 32);
         const i32x4 pw = {(int)wv.pk[4 * chunk], (int)wv.pk[4 * chunk + 1], (int)wv.pk[4 * chunk + 2],
@@ -513,7 +533,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
     } else {
       const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
       const f32x16 acc = kk == 0 ? zero16() : wv.s[blk];
-      if constexpr (FP8)
+      if constexpr (FP8 && BS)
+        wv.s[blk] = blk < 2 ? mfma_fp8_32x32x64_sa<0>(a, wv.q[kk], acc, (int)kexp)
+                            : mfma_fp8_32x32x64_sa<1>(a, wv.q[kk], acc, (int)kexp);
+      else if constexpr (FP8)
         wv.s[blk] = mfma_fp8_32x32x64(a, wv.q[kk], acc);
       else
         wv.s[blk] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), wv.q[kk], acc);
@@ -552,8 +575,13 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
     // product multiplies the zero probabilities the item starts with (by a
     // zero-filled or fully loaded V buffer), and at step s_hi the scores of a
     // tile the wave does not need are computed and never read.
-    if (pstep >= s_lo && pstep <= s_hi)
+    if (pstep >= s_lo && pstep <= s_hi) {
+      if constexpr (BS) {
+        kexp = ebuf[tile_of(pstep)];
+        vexp = ebuf[tile_of(pstep - 1)];
+      }
       run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
+    }
   };
 
   // ---- vector work of step pstep: online softmax of S_pstep -> probabilities.
@@ -635,8 +663,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
     }
   };
 
-  // ---- prologue: K tile 0 into buffer 0; V buffer 1 (read by the empty P.V
-  // product of step 0) and the probabilities start at zero.
+  // ---- prologue: the tiles' scale exponents (block scales) into LDS; K tile 0
+  // into buffer 0; V buffer 1 (read by the empty P.V product of step 0) and the
+  // probabilities start at zero.
+  if constexpr (BS) {
+    // word t: E8M0 of K blocks 2t, 2t+1 and V blocks 2t, 2t+1 (indices past the
+    // last block repeat it: those keys load as zeros and are masked)
+    const int nbk = (Nk + 63) / 64;
+    const float* ksc = p.k_scale + ((size_t)b * p.Hkv + g) * nbk;
+    const float* vsc = p.v_scale + ((size_t)b * p.Hkv + g) * nbk;
+    for (int t = tid; t <= T; t += kThreads) {
+      const int i0 = min(2 * t, nbk - 1), i1 = min(2 * t + 1, nbk - 1);
+      const uint32_t k0 = __float_as_uint(ksc[i0]), k1 = __float_as_uint(ksc[i1]);
+      const uint32_t v0 = __float_as_uint(vsc[i0]), v1 = __float_as_uint(vsc[i1]);
+      ebuf[t] = ((k0 >> 23) & 0xffu) | (((k1 >> 23) & 0xffu) << 8) | (((v0 >> 23) & 0xffu) << 16) |
+                (((v1 >> 23) & 0xffu) << 24);
+    }
+  }
   issue_k(tile_of(0), 0);
 #pragma unroll
   for (int i = 0; i < C::V_TILE / (16 * kThreads); ++i)
@@ -719,10 +762,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, in
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
 // tiles instead of one stream each.
-template <int DQK, int DV, bool FP8>
+template <int DQK, int DV, bool FP8, bool BS>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
   const int nqt = (p.Nq + kBM - 1) / kBM;
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
@@ -738,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
     const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
     const int j = u % per_bh;
     const int qt = half == 0 ? nqt - 1 - j : j;
-    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8>(p, smem, bh, qt, !single && half == 1);
+    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8, BS>(p, smem, ebuf, bh, qt, !single && half == 1);
     if (single) {
       u += nrank;
     } else {
@@ -778,20 +822,24 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
   const int grid = tiles <= cu_count[dev] ? (int)tiles : (int)std::min<long long>(units, cu_count[dev]);
   const dim3 g(grid), blk(kThreads);
   if (d_v != 128) return hipErrorInvalidValue;
+  if (d_qk != 128 && d_qk != 192) return hipErrorInvalidValue;
   if (dtype == 0) {
+    if (p.block64) return hipErrorInvalidValue;
     if (d_qk == 128)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, false>), g, blk, 0, stream, p);
-    else if (d_qk == 192)
-      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, false>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, false, false>), g, blk, 0, stream, p);
     else
-      return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, false, false>), g, blk, 0, stream, p);
+  } else if (p.block64) {
+    if (p.Nk > kBlock64MaxKeys) return hipErrorInvalidValue;
+    if (d_qk == 128)
+      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, true>), g, blk, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, true>), g, blk, 0, stream, p);
   } else {
     if (d_qk == 128)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true>), g, blk, 0, stream, p);
-    else if (d_qk == 192)
-      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, false>), g, blk, 0, stream, p);
     else
-      return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, false>), g, blk, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -40,6 +40,15 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// As mfma_fp8_32x32x64 with the A operand scaled by 2^(E - 127), E = byte SEL
+// of scale_a (an E8M0 exponent).  Each lane's byte scales the 32 k-slots of A
+// it supplies; with the same word in every lane the whole A block gets one
+// power-of-two scale, applied exactly inside the instruction.
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64_sa(i32x8 a, i32x8 b, f32x16 c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, scale_a, 0, 127);
+}
+
 // D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), unit block scales.  Lane l
 // supplies 32 k-slots of A row / B column (l % 16); lane group l / 16 selects
 // which quarter of the 128 k-slots.  D: lane l holds column (l % 16), rows

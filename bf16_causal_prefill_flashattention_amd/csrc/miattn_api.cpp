@@ -43,7 +43,7 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, co
 
 int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                  int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
-                 const float* v_scale, double tau, void* stream) {
+                 const float* v_scale, double tau, void* stream, bool block64 = false) {
   miattn::AttnParams p;
   p.q = q;
   p.k = k;
@@ -59,6 +59,7 @@ int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.Nq = Nq;
   p.Nk = Nk;
   p.sm_scale_log2 = (float)(1.4426950408889634 * tau);  // log2-domain softmax scale
+  p.block64 = block64 ? 1 : 0;
   const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
@@ -69,7 +70,6 @@ int validate_quantize(const void* x, int x_dtype, void* y, float* scale, int B, 
   if (hadamard != 0 && hadamard != 1) return MIATTN_ERR_DTYPE;
   if (B < 0 || N < 0 || H < 1) return MIATTN_ERR_SIZE;
   if (d != 128 && d != 192) return MIATTN_ERR_SHAPE;
-  if (hadamard && d != 128) return MIATTN_ERR_SHAPE;
   if (B == 0) return MIATTN_OK;
   if (!scale) return MIATTN_ERR_NULL;
   if (N > 0 && (!x || !y)) return MIATTN_ERR_NULL;
@@ -93,7 +93,7 @@ const char* attn_status_string(int status) {
     case MIATTN_OK: return "success";
     case MIATTN_ERR_NULL: return "a required pointer is NULL";
     case MIATTN_ERR_SIZE: return "invalid size (negative, zero head count, Hq not a multiple of Hkv, Nq > Nk, or too large)";
-    case MIATTN_ERR_SHAPE: return "unsupported head dimensions (need (128,128) or (192,128); Hadamard needs d=128)";
+    case MIATTN_ERR_SHAPE: return "unsupported head dimensions (need (128,128) or (192,128); the quantizer needs d in {128, 192})";
     case MIATTN_ERR_DTYPE: return "unknown dtype, source type or flag value";
     case MIATTN_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
     case MIATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales and lse 4-byte alignment)";
@@ -129,6 +129,30 @@ int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int
   if (st != MIATTN_OK || B == 0) return st;
   const hipError_t e =
       miattn::launch_quantize_fp8(x, x_dtype, x_fp8, scale, B, H, N, d, hadamard != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale,
+                     const float* v_scale, float softmax_scale, void* stream) {
+  if (!(softmax_scale == 0.0f || (std::isfinite(softmax_scale) && softmax_scale > 0.0f))) return MIATTN_ERR_VALUE;
+  const int st = validate_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale,
+                                   k_scale, v_scale);
+  if (st != MIATTN_OK) return st;
+  if (Nk > miattn::kBlock64MaxKeys) return MIATTN_ERR_SIZE;
+  if (B == 0 || Nq == 0) return MIATTN_OK;
+  const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
+  return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale, k_scale,
+                      v_scale, tau, stream, true);
+}
+
+int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,
+                              int hadamard, void* stream) {
+  const int st = validate_quantize(x, x_dtype, x_fp8, scale, B, H, N, d, hadamard);
+  if (st != MIATTN_OK || B == 0 || N == 0) return st;
+  if ((double)B * H * ((N + 63) / 64) > 2147483647.0) return MIATTN_ERR_SIZE;  // one workgroup per block
+  const hipError_t e = miattn::launch_quantize_fp8_block64(x, x_dtype, x_fp8, scale, B, H, N, d, hadamard != 0,
+                                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
 

@@ -19,6 +19,12 @@ Recipe (one torch CPU generator per tensor, fp32 N(0, 1)):
   (a random permutation's first c entries), multiply those channels by
   ``outlier_gain`` in K[:, :, g] and in Q[:, :, h] for every query head h of g's
   group (aligned channels).  V stays N(0, 1).
+  With ``kv_decades = D > 0``: every position n of every batch b gets a gain
+  10^(-D * u[b, n]), u ~ Uniform[0, 1) from seed + 4, applied to its K and V
+  rows of all heads (magnitudes that drift along the sequence, the case finer
+  FP8 scale granularity is for).
+  ``scales`` names the FP8 scale granularity a workload is quantized with:
+  "head" (one scale per batch and head) or "block64" (one per 64 positions).
 """
 
 from __future__ import annotations
@@ -42,6 +48,8 @@ class Workload:
     outlier_gain: float = 20.0
     hadamard: bool = False
     seed: int = 0
+    kv_decades: float = 0.0
+    scales: str = "head"
     note: str = field(default="", compare=False)
 
     @property
@@ -76,6 +84,8 @@ WORKLOADS = {
     "fp8_gqa_n16k_had": _w("fp8_gqa_n16k_had", "fp8", 1, 32, 8, 16384, 128, 128,
                            outliers=4, hadamard=True),
     "fp8_mla_n32k": _w("fp8_mla_n32k", "fp8", 1, 16, 16, 32768, 192, 128),
+    "fp8_mha_n32k_block64": _w("fp8_mha_n32k_block64", "fp8", 1, 32, 32, 32768, 128, 128, scales="block64",
+                               note="the FP8 headline shape with per-64-position scales"),
 }
 
 
@@ -112,6 +122,13 @@ def make_qkv(w: Workload):
                 k[b, :, g, c] *= w.outlier_gain
                 for h in range(g * grp, (g + 1) * grp):
                     q[b, :, h, c] *= w.outlier_gain
+    if w.kv_decades:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(int(w.seed) + 4)
+        u = torch.rand((w.B, w.N), generator=g, dtype=torch.float32)
+        gain = torch.pow(torch.tensor(10.0), -w.kv_decades * u)[:, :, None, None]
+        k *= gain
+        v *= gain
     return q, k, v
 
 

@@ -20,7 +20,7 @@
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 2
+#define MIATTN_ABI_VERSION 3
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -34,7 +34,7 @@ extern "C" {
 #define MIATTN_OK 0
 #define MIATTN_ERR_NULL (-1)     /* a required pointer is NULL */
 #define MIATTN_ERR_SIZE (-2)     /* a size is negative, zero where it may not be, Hq % Hkv != 0, Nq > Nk, or too large */
-#define MIATTN_ERR_SHAPE (-3)    /* unsupported head dimensions, or Hadamard with d != 128 */
+#define MIATTN_ERR_SHAPE (-3)    /* unsupported head dimensions */
 #define MIATTN_ERR_DTYPE (-4)    /* unknown dtype / source type code, or a flag outside {0, 1} */
 #define MIATTN_ERR_HIP (-5)      /* the HIP runtime reported an error when enqueuing */
 #define MIATTN_ERR_ALIGN (-6)    /* a tensor pointer is not 16-byte aligned (scales, lse: 4-byte) */
@@ -120,18 +120,81 @@ int attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float
  * scale  [B, H] fp32, written with the per-(batch, head) scale; it is also used
  *        as the amax accumulator while the call's kernels run, so it must not
  *        alias x or x_fp8.
- * Steps, each in fp32: y = x (or the unnormalised Sylvester transform x H_128
- * with butterfly stages of width 1, 2, ..., 64 when hadamard = 1);
+ * Steps, each in fp32: y = x, or with hadamard = 1 the unnormalised Sylvester
+ * transform of the channels (d = 128: x H_128, butterfly stages of width 1, 2,
+ * ..., 64; d = 192: H_64 on each of the three groups of 64 channels, stages
+ * 1, ..., 32 -- the pages show the rotation at d = 128 only);
  * amax = max |y| over the (b, h) slice; inv = 448 / amax; code =
  * round-to-nearest-even e4m3(clamp(y * inv, -448, 448)); scale = amax / 448,
- * times fp32(2^-3.5) when hadamard = 1 (the 1/sqrt(128) normalisation).
- * amax == 0 gives inv = 1, scale = 1 (times fp32(2^-3.5) with hadamard), all
- * codes 0.  The dequantized value code * scale is what attn_fwd consumes.
- * Sizes: B >= 0, N >= 0, H >= 1, d in {128, 192}; hadamard in {0, 1} and
- * hadamard = 1 requires d = 128.  B == 0 is an empty call; N == 0 writes the
- * scales only.  Deterministic.  Returns MIATTN_OK or MIATTN_ERR_*. */
+ * times the normalisation when hadamard = 1 (fp32(2^-3.5) for d = 128, 2^-3
+ * for d = 192).  amax == 0 gives inv = 1, scale = 1 (times the normalisation
+ * with hadamard), all codes 0.  The dequantized value code * scale is what
+ * attn_fwd consumes.
+ * Sizes: B >= 0, N >= 0, H >= 1, d in {128, 192}; hadamard in {0, 1}.
+ * B == 0 is an empty call; N == 0 writes the scales only.  Deterministic.
+ * Returns MIATTN_OK or MIATTN_ERR_*. */
 int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,
                       int hadamard, void* stream);
+
+/* Per-64-position FP8 e4m3fn quantization with power-of-two scales.
+ *
+ * Defines: the finer scaling granularity the pages name as a lever on FP8
+ * accuracy ([P1] "ZYFA's performance and accuracy data": per-tensor or
+ * per-head scales, block-wise scaling, scaling granularity): one scale per
+ * (batch, head, block of 64 consecutive positions).  The scales are powers of
+ * two, the form the scaled matrix instructions of CDNA4 apply exactly, so
+ * attn_fwd_block64 applies the K and V block scales inside its MFMAs.
+ *
+ * x      [B, N, H, d] contiguous, fp32 (MIATTN_SRC_FP32) or bf16
+ *        (MIATTN_SRC_BF16), read only.
+ * x_fp8  [B, N, H, d] contiguous uint8, written with the e4m3fn codes.
+ * scale  [B, H, ceil(N / 64)] fp32, written: scale[b, h, j] = 2^e covers
+ *        positions 64j .. 64j + 63 (the last block may be shorter).
+ * Steps, each in fp32: z = x, or with hadamard = 1 z = (x H) * norm with the
+ * rotation and normalisation of attn_quantize_fp8 (the normalisation goes into
+ * the values: a power of two cannot hold 2^-3.5); amax = max |z| over the
+ * block; e = the smallest integer with amax <= 448 * 2^e, but at least -126
+ * (e = 0 when amax == 0); code = round-to-nearest-even e4m3(z * 2^-e), which
+ * never exceeds 448.  The dequantized value is code * scale[b, h, n / 64].
+ * Sizes as attn_quantize_fp8 (d in {128, 192}, hadamard in {0, 1}); B == 0
+ * or N == 0 is an empty call.  x is read once.  Deterministic.
+ * Returns MIATTN_OK or MIATTN_ERR_*. */
+int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,
+                              int hadamard, void* stream);
+
+/* FP8 causal attention with per-64-position scales (one chunk of a chunked
+ * prefill, as attn_fwd_chunk).
+ *
+ * Defines: the causal forward attention of attn_fwd / attn_fwd_chunk (see
+ * there for the pages' passages) on FP8 e4m3 inputs whose scales change every
+ * 64 positions ([P1] "ZYFA's performance and accuracy data", scaling
+ * granularity).  The K and V block scales are applied as E8M0 exponents by the
+ * scaled MFMAs of CDNA4 (the pages' kernel uses those instructions to undo
+ * power-of-two block scales, [P3] "ZYFA 如何工作？"), so they cost no vector
+ * work; Q's block scale is folded into the score multiplier.
+ *
+ * Layout (contiguous BSHD, e4m3fn codes, as attn_fwd_chunk):
+ *   q [B, Nq, Hq, d_qk], k [B, Nk, Hkv, d_qk], v [B, Nk, Hkv, d_v] (uint8)
+ *   q_scale [B, Hq,  ceil(Nq / 64)]  fp32, positive (any value)
+ *   k_scale [B, Hkv, ceil(Nk / 64)]  fp32, each a power of two in [2^-126, 2^127]
+ *   v_scale [B, Hkv, ceil(Nk / 64)]  fp32, each a power of two in [2^-126, 2^127]
+ *   out [B, Nq, Hq, d_v] bfloat16 (written); lse [B, Hq, Nq] fp32 (written
+ *   unless NULL).  The real inputs are code * scale of the element's block
+ *   (blocks of q count query rows, blocks of k and v count key rows).
+ * K and V scales are read through their exponent bits only: a value that is
+ * not a power of two acts as the power of two below it.  The quantizer
+ * attn_quantize_fp8_block64 writes exactly this form.
+ * Query row i sits at position i + Nk - Nq and attends to keys
+ * j <= i + Nk - Nq; softmax_scale: tau, 0 selects 1 / sqrt(d_qk), otherwise
+ * finite and positive (else MIATTN_ERR_VALUE).
+ * Sizes: B >= 0, 0 <= Nq <= Nk <= 2^20 (the exponents of a query tile's keys
+ * are staged on chip), Hq >= 1, Hkv >= 1, Hq % Hkv == 0, (d_qk, d_v) in
+ * {(128, 128), (192, 128)}; B == 0 or Nq == 0 is an empty call.  Alignment,
+ * stream, asynchrony and determinism as attn_fwd.
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale,
+                     const float* v_scale, float softmax_scale, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

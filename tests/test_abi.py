@@ -32,9 +32,10 @@ def lib():
     return pkg.load_library()
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_seven_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["attn_fwd", "attn_fwd_chunk", "attn_quantize_fp8", "attn_status_string", "attn_version"])
+        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_quantize_fp8", "attn_quantize_fp8_block64",
+         "attn_status_string", "attn_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -101,12 +102,39 @@ def quant(lib, x=P, src=0, y=P, s=P, B=1, H=2, N=8, d=128, had=0):
     (dict(x=None), E_NULL), (dict(y=None), E_NULL), (dict(s=None), E_NULL),
     (dict(src=2), E_DTYPE), (dict(had=2), E_DTYPE),
     (dict(B=-1), E_SIZE), (dict(H=0), E_SIZE), (dict(N=-1), E_SIZE),
-    (dict(d=64), E_SHAPE), (dict(d=192, had=1), E_SHAPE),
+    (dict(d=64), E_SHAPE), (dict(d=256, had=1), E_SHAPE),
     (dict(x=P + 4), E_ALIGN), (dict(s=P + 1), E_ALIGN),
     (dict(B=0), OK),
 ])
 def test_quantize_validation(lib, kw, expect):
     assert quant(lib, **kw) == expect
+    # the per-64-position quantizer validates the same way
+    assert lib.attn_quantize_fp8_block64(*[kw.get(n, dv) for n, dv in (
+        ("x", P), ("src", 0), ("y", P), ("s", P), ("B", 1), ("H", 2), ("N", 8), ("d", 128), ("had", 0))],
+        None) == expect
+
+
+def test_quantize_block64_empty_sequence(lib):
+    assert lib.attn_quantize_fp8_block64(P, 0, P, P, 1, 2, 0, 128, 0, None) == OK
+
+
+def block64(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=128, dv=128, qs=P, ks=P, vs=P,
+            tau=0.0):
+    return lib.attn_fwd_block64(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, qs, ks, vs, tau, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), E_NULL), (dict(o=None), E_NULL), (dict(qs=None), E_NULL), (dict(ks=None), E_NULL),
+    (dict(vs=None), E_NULL),
+    (dict(Nq=21), E_SIZE), (dict(Nq=-1), E_SIZE), (dict(Hq=3, Hkv=2), E_SIZE),
+    (dict(Nq=8, Nk=(1 << 20) + 1), E_SIZE),
+    (dict(dqk=64), E_SHAPE), (dict(dqk=192, dv=192), E_SHAPE),
+    (dict(lse=P + 2), E_ALIGN), (dict(ks=P + 2), E_ALIGN), (dict(k=P + 4), E_ALIGN),
+    (dict(tau=-0.5), E_VALUE), (dict(tau=float("nan")), E_VALUE),
+    (dict(Nq=0), OK), (dict(B=0), OK), (dict(Nq=0, q=None, k=None, v=None, o=None), OK),
+])
+def test_attn_fwd_block64_validation(lib, kw, expect):
+    assert block64(lib, **kw) == expect
 
 
 def test_binding_refuses_cpu_tensors():
@@ -119,6 +147,14 @@ def test_binding_refuses_cpu_tensors():
         pkg.attn_fwd_chunk(q, q, q)
     with pytest.raises(ValueError):
         pkg.attn_quantize_fp8(q.float())
+    with pytest.raises(ValueError):
+        pkg.attn_quantize_fp8_block64(q.float())
+    c = torch.zeros(1, 4, 1, 128, dtype=torch.uint8)
+    s = torch.ones(1, 1, 1)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_block64(c, c, c, s, s, s)
+    with pytest.raises(TypeError):
+        pkg.attn_fwd_block64(q, q, q, s, s, s)
 
 
 def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
@@ -133,5 +169,7 @@ def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
         pkg.flash_attn_func(q.float(), q.float(), q.float())
     with pytest.raises(ValueError):
         pkg.flash_attn_func(q, q, q, hadamard=True)
+    with pytest.raises(ValueError):
+        pkg.flash_attn_func(q, q, q, fp8=True, fp8_scales="tensor")
     with pytest.raises(ValueError):  # CPU tensors
         pkg.flash_attn_func(q, q, q)

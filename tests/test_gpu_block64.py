@@ -1,0 +1,227 @@
+"""GPU FP8 path with per-64-position scales (``attn_quantize_fp8_block64`` and
+``attn_fwd_block64`` through the C ABI), and the Hadamard rotation at head
+dimension 192, against the oracle.
+
+* Quantizers: codes and scales bit-identical to the oracle's (the exponent and
+  the codes are decided by the same fp32 steps on both sides).
+* Attention: the oracle quantizes on the CPU and the same codes and scales are
+  uploaded, so the oracle's inputs never come from the GPU; output relative
+  Frobenius error <= 6e-2 and the LSE within the lean-P / FP8-MFMA bound of the
+  chunk tests, against the fp64 oracle on the dequantized inputs.
+* With every block scale of a (batch, head) equal to one power of two, the
+  block-scaled kernel must reproduce the per-head kernel bit for bit: a
+  power-of-two scale applied inside the MFMA commutes with every rounding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bf16_causal_prefill_flashattention_amd as miattn
+from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS, Workload, make_qkv
+from oracle import (
+    attn_chunk_ref_rows,
+    attn_ref,
+    dequantize_block64_ref,
+    dequantize_ref,
+    quantize_block64_ref,
+    quantize_ref,
+)
+from parity_util import TOL, rel_fro, sample_rows
+from test_gpu_chunk import _check_lse
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(shape, seed, scale=1.0, decades=0.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g) * scale
+    if decades:
+        x *= torch.pow(torch.tensor(10.0), -decades * torch.rand(shape[0], shape[1], 1, 1, generator=g))
+    return x
+
+
+def _same_bits(a, b, name):
+    assert a.shape == b.shape, (name, a.shape, b.shape)
+    if a.dtype == np.float32:
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+    else:
+        n = np.count_nonzero(a != b)
+        assert n == 0, f"{name}: {n} of {a.size} differ"
+
+
+# ---- quantizers
+
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [128, 192])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300, 1000])
+def test_block64_quantize_bit_exact(require_gpu, hadamard, src, d, N):
+    x = _x((2, N, 3, d), 11 * N + d + hadamard, 3.0, decades=4.0)
+    if src == "bf16":
+        x = x.to(torch.bfloat16)
+    codes, scales = miattn.attn_quantize_fp8_block64(x.cuda(), hadamard=hadamard)
+    torch.cuda.synchronize()
+    rc, rs = quantize_block64_ref(x, hadamard)
+    _same_bits(scales.cpu().numpy(), rs, "scales")
+    _same_bits(codes.cpu().numpy(), rc, "codes")
+
+
+def test_block64_quantize_zero_tiny_and_huge_blocks(require_gpu):
+    x = _x((1, 320, 2, 128), 5)
+    x[0, 64:128] = 0
+    x[0, 128:192] *= 1e-40  # fp32 subnormals: exponent clamped at -126
+    x[0, 192:256] *= 1e30
+    x[0, 256:320, 1] *= 2.0 ** -120
+    codes, scales = miattn.attn_quantize_fp8_block64(x.cuda())
+    torch.cuda.synchronize()
+    rc, rs = quantize_block64_ref(x)
+    _same_bits(scales.cpu().numpy(), rs, "scales")
+    _same_bits(codes.cpu().numpy(), rc, "codes")
+    assert rs[0, 0, 1] == 1.0 and rs[0, 0, 2] == np.float32(2.0 ** -126)
+
+
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+@pytest.mark.parametrize("N", [1, 255, 257, 1000])
+def test_per_head_hadamard_d192_bit_exact(require_gpu, src, N):
+    x = _x((2, N, 3, 192), N + 3, 2.0)
+    if src == "bf16":
+        x = x.to(torch.bfloat16)
+    codes, scales = miattn.attn_quantize_fp8(x.cuda(), hadamard=True)
+    torch.cuda.synchronize()
+    rc, rs = quantize_ref(x, True)
+    _same_bits(scales.cpu().numpy(), rs, "scales")
+    _same_bits(codes.cpu().numpy(), rc, "codes")
+
+
+# ---- attention with block scales
+
+def _inputs(B, Nq, Nk, Hq, Hkv, dqk, outl, decades, had, seed):
+    w = Workload("b64", "fp8", B, Hq, Hkv, Nk, dqk, 128, outliers=outl, seed=seed, kv_decades=decades)
+    q, k, v = make_qkv(w)
+    q = q[:, Nk - Nq:].contiguous()
+    (cq, sq), (ck, sk), (cv, sv) = (quantize_block64_ref(q, had), quantize_block64_ref(k, had),
+                                    quantize_block64_ref(v, False))
+    ref_in = (dequantize_block64_ref(cq, sq), dequantize_block64_ref(ck, sk), dequantize_block64_ref(cv, sv))
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
+    return (q, k, v), dev, ref_in
+
+
+CASES = [
+    # (B, Nq, Nk, Hq, Hkv, d_qk, outliers, kv_decades, hadamard)
+    (1, 512, 512, 2, 2, 128, 0, 0.0, False),
+    (2, 1, 1, 2, 1, 128, 0, 0.0, False),
+    (1, 129, 129, 4, 2, 128, 0, 3.0, False),
+    (1, 700, 700, 4, 4, 128, 4, 2.0, True),
+    (1, 1000, 1000, 8, 2, 128, 4, 3.0, False),
+    (1, 333, 333, 2, 2, 192, 0, 3.0, False),
+    (1, 1000, 1000, 4, 4, 192, 0, 0.0, True),
+    (1, 300, 1000, 4, 2, 128, 0, 3.0, False),
+    (1, 64, 2048, 2, 2, 192, 0, 2.0, False),
+]
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,dqk,outl,dec,had", CASES)
+def test_block64_attention_matches_oracle(require_gpu, B, Nq, Nk, Hq, Hkv, dqk, outl, dec, had):
+    _, dev, ref_in = _inputs(B, Nq, Nk, Hq, Hkv, dqk, outl, dec, had, seed=Nq + 3 * Nk + Hq)
+    out, lse = miattn.attn_fwd_block64(*dev)
+    torch.cuda.synchronize()
+    ref, ref_lse = attn_chunk_ref_rows(*ref_in)
+    err = rel_fro(out.cpu(), ref)
+    assert err <= TOL["fp8"], err
+    assert torch.isfinite(out.float()).all()
+    _check_lse("fp8", lse.cpu().numpy().astype(np.float64), ref_lse, ref_in)
+
+
+def test_block64_scales_are_applied(require_gpu):
+    # K and V magnitudes rising over six decades along the sequence: the early
+    # queries see only tiny keys and values, which one scale per head (set by
+    # the late, large positions) pushes into e4m3's subnormal range, while
+    # per-64-position scales keep them at full relative precision.  Errors are
+    # measured against attention on the exact fp32 inputs, over the first
+    # quarter of the rows.
+    B, N, H, d = 1, 1024, 4, 128
+    g = torch.Generator().manual_seed(21)
+    q, k, v = (torch.randn(B, N, H, d, generator=g) for _ in range(3))
+    gain = torch.pow(torch.tensor(10.0), -6.0 * (1.0 - torch.arange(N, dtype=torch.float32) / N))
+    k *= gain[None, :, None, None]
+    v *= gain[None, :, None, None]
+    (cq, sq), (ck, sk), (cv, sv) = (quantize_block64_ref(t) for t in (q, k, v))
+    out_b, _ = miattn.attn_fwd_block64(*[torch.from_numpy(np.ascontiguousarray(a)).cuda()
+                                         for a in (cq, ck, cv, sq, sk, sv)], with_lse=False)
+    (cq, sq), (ck, sk), (cv, sv) = (quantize_ref(t) for t in (q, k, v))
+    out_h = miattn.attn_fwd(*[torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)])
+    torch.cuda.synchronize()
+    exact = attn_ref(q, k, v)[:, : N // 4]
+    e_b, e_h = rel_fro(out_b.cpu()[:, : N // 4], exact), rel_fro(out_h.cpu()[:, : N // 4], exact)
+    assert e_b <= TOL["fp8"] and e_h > 0.2 and e_b < 0.25 * e_h, (e_b, e_h)
+
+
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk):
+    B, Nq, Nk, Hq, Hkv = 1, 500, 900, 4, 2
+    g = np.random.default_rng(dqk)
+    codes = [g.integers(0, 256, size=s, dtype=np.uint8) for s in
+             ((B, Nq, Hq, dqk), (B, Nk, Hkv, dqk), (B, Nk, Hkv, 128))]
+    for c in codes:
+        c[(c & 0x7F) == 0x7F] = 0x00  # no NaN codes
+    sq = g.uniform(0.001, 0.01, (B, Hq)).astype(np.float32)
+    sk = np.float32(2.0) ** g.integers(-9, -3, (B, Hkv)).astype(np.float32)
+    sv = np.float32(2.0) ** g.integers(-9, -3, (B, Hkv)).astype(np.float32)
+    nbq, nbk = (Nq + 63) // 64, (Nk + 63) // 64
+    blocks = [np.repeat(sq[:, :, None], nbq, 2), np.repeat(sk[:, :, None], nbk, 2), np.repeat(sv[:, :, None], nbk, 2)]
+    cdev = [torch.from_numpy(c).cuda() for c in codes]
+    out_h, lse_h = miattn.attn_fwd_chunk(*cdev, *[torch.from_numpy(s).cuda() for s in (sq, sk, sv)])
+    out_b, lse_b = miattn.attn_fwd_block64(*cdev, *[torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in blocks])
+    torch.cuda.synchronize()
+    assert torch.equal(out_h.view(torch.int16), out_b.view(torch.int16))
+    assert torch.equal(lse_h.view(torch.int32), lse_b.view(torch.int32))
+
+
+def test_block64_deterministic_and_writes_only_its_outputs(require_gpu):
+    _, dev, _ = _inputs(1, 1000, 1000, 8, 2, 128, 4, 3.0, False, seed=5)
+    B, Nq, Hq = 1, 1000, 8
+    guard = 4096
+    obuf = torch.full((2 * guard + B * Nq * Hq * 128,), -7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((2 * guard + B * Hq * Nq,), -7.0, dtype=torch.float32, device="cuda")
+    out = obuf[guard:guard + B * Nq * Hq * 128].view(B, Nq, Hq, 128)
+    lse = lbuf[guard:guard + B * Hq * Nq].view(B, Hq, Nq)
+    miattn.attn_fwd_block64(*dev, out=out, lse=lse)
+    first_o, first_l = out.clone(), lse.clone()
+    for _ in range(20):
+        miattn.attn_fwd_block64(*dev, out=out, lse=lse)
+        assert torch.equal(out.view(torch.int16), first_o.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), first_l.view(torch.int32))
+    torch.cuda.synchronize()
+    for buf in (obuf, lbuf):
+        assert bool((buf[:guard].float() == -7.0).all()) and bool((buf[-guard:].float() == -7.0).all())
+
+
+def test_block64_flash_attn_func(require_gpu):
+    w = Workload("fa", "fp8", 1, 4, 2, 700, 128, 128, outliers=4, seed=9, kv_decades=2.0)
+    q, k, v = (t.to(torch.bfloat16) for t in make_qkv(w))
+    out, lse = miattn.flash_attn_func(q.cuda(), k.cuda(), v.cuda(), fp8=True, fp8_scales="block64",
+                                      hadamard=True, return_lse=True)
+    torch.cuda.synchronize()
+    exact = attn_ref(q, k, v)
+    assert rel_fro(out.cpu(), exact) <= TOL["fp8"]
+    assert lse.shape == (1, 4, 700)
+
+
+def test_block64_full_size_sampled_rows(require_gpu):
+    # the FP8 headline shape (B=1, H=32, N=32768, d=128) with per-64-position
+    # scales, quantized on the GPU from bf16 activations in the benchmark's
+    # launch configuration; sampled rows of sampled heads against the oracle on
+    # the dequantized codes (the quantizer itself is pinned bit-exact above)
+    w = WORKLOADS["fp8_mha_n32k_block64"]
+    q, k, v = (t.to(torch.bfloat16) for t in make_qkv(w))
+    (cq, sq), (ck, sk), (cv, sv) = (miattn.attn_quantize_fp8_block64(t.cuda()) for t in (q, k, v))
+    out, _ = miattn.attn_fwd_block64(cq, ck, cv, sq, sk, sv, with_lse=False)
+    torch.cuda.synchronize()
+    heads = [0, 13, 31]
+    rows = sample_rows(w.N, 24, seed=3)
+    sl = lambda c, s, hh: dequantize_block64_ref(c[:, :, hh].cpu().numpy(), s[:, hh].cpu().numpy())
+    for h in heads:
+        ref, _ = attn_chunk_ref_rows(sl(cq, sq, [h]), sl(ck, sk, [h]), sl(cv, sv, [h]), rows=rows)
+        got = out[:, rows][:, :, [h]].cpu()
+        assert rel_fro(got, ref) <= TOL["fp8"], (h, rel_fro(got, ref))
