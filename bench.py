@@ -434,7 +434,6 @@ def main(argv=None):
             "front_end_ms": round(front_q, 4),
             "roofline": roofline(wq, attn_q),
         }
-        rec["block64"]["roofline"]["traffic"] = None
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
         msc, attn_c = run_chunk(w, Nq, args.steps, args.warmup)

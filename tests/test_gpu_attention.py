@@ -81,8 +81,6 @@ def test_bf16_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl):
 @pytest.mark.parametrize("B,N,Hq,Hkv,dqk,outl", SMALL)
 @pytest.mark.parametrize("hadamard", [False, True])
 def test_fp8_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl, hadamard):
-    if hadamard and dqk != 128:
-        pytest.skip("the Hadamard rotation is defined for d = 128")
     w = Workload("t", "fp8", B, Hq, Hkv, N, dqk, 128, outliers=outl, seed=N + Hq + 1)
     q, k, v = make_qkv(w)
     out, gpu_codes = _fp8_gpu(q, k, v, hadamard)
@@ -92,6 +90,36 @@ def test_fp8_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl, hadamard)
     ref = attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
     err = rel_fro(out, ref)
     assert err <= TOL["fp8"], (err, per_head_rel_fro(out, ref))
+
+
+PAIRED = [
+    # (dtype, B, N, Hq, Hkv, d_qk): more 256-query tiles than CUs, so every
+    # persistent workgroup runs pairs of tiles, the lighter tile of a pair with
+    # its keys walked downward; an odd tile count leaves a middle tile unpaired
+    ("bf16", 1, 1280, 64, 8, 128),
+    ("fp8", 1, 1280, 64, 8, 128),
+    ("fp8", 1, 1100, 64, 16, 192),
+    ("bf16", 2, 1100, 32, 32, 192),
+]
+
+
+@pytest.mark.parametrize("dtype,B,N,Hq,Hkv,dqk", PAIRED)
+def test_paired_persistent_full_compare(require_gpu, dtype, B, N, Hq, Hkv, dqk):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * Hq * ((N + 255) // 256) > cus, "the case must launch in paired mode"
+    w = Workload("t", dtype, B, Hq, Hkv, N, dqk, 128, outliers=4, seed=N + Hq + B)
+    if dtype == "bf16":
+        out, (q, k, v) = _bf16_case(w)
+        ref = attn_ref(q, k, v)
+    else:
+        q, k, v = make_qkv(w)
+        out, gpu_codes = _fp8_gpu(q, k, v, False)
+        ref_codes = _fp8_oracle_inputs(q, k, v, False)
+        _assert_same_codes(gpu_codes, ref_codes)
+        cq, sq, ck, sk, cv, sv = ref_codes
+        ref = attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
+    err = per_head_rel_fro(out, ref)
+    assert rel_fro(out, ref) <= TOL[dtype] and err.max() <= TOL[dtype], err
 
 
 def _heads_to_sample(w: Workload):
