@@ -19,8 +19,8 @@
 //
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
 // (batch, query head); each wave owns 32 queries.  Key tiles hold 128 keys
-// (FP8) or 64 keys (BF16); a wave skips the tiles wholly above its queries and
-// masks only the tiles that cross its diagonal.
+// (FP8), 96 (BF16, d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips the tiles
+// wholly above its queries and masks only the tiles that cross its diagonal.
 //
 // Matrix layout.  A wave computes S^T = K_tile * Q^T (keys on MFMA rows,
 // queries on MFMA columns), so lane l owns query (l % 32) and holds half of the
@@ -89,7 +89,12 @@ constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 template <bool FP8, int DQK, int DV>
 struct Cfg {
   static constexpr int EB = FP8 ? 1 : 2;     // bytes per element
-  static constexpr int BN = FP8 ? 128 : 64;  // keys per tile
+  // keys per tile.  A phase carries a roughly fixed cost (barriers, the first
+  // operand reads), so larger tiles amortise it; BF16 at d = 128 stops at 96
+  // keys (128 would not fit two waves' registers per SIMD), and BF16 at d = 192
+  // stays at 64 (its 384-byte K rows would not split into whole 1 KB load
+  // blocks per wave at 96)
+  static constexpr int BN = FP8 ? 128 : (DQK == 128 ? 96 : 64);
   static constexpr int NBLK = BN / 32;       // 32-key MFMA blocks per tile
   static constexpr int KROW = DQK * EB;      // bytes of one K row
   static constexpr int VROW = DV * EB;       // bytes of one V row
