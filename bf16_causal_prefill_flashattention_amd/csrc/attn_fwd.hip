@@ -76,6 +76,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace miattn {
@@ -810,21 +811,25 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
   if (p.Nq < 1 || p.Nk < p.Nq) return hipErrorInvalidValue;
   const long long units = attn_fwd_units(p.B, p.Hq, p.Nq);
   if (units <= 0 || units > 0x7fffffffLL) return hipErrorInvalidValue;
-  static int cu_count[64];  // per device, filled on first use
+  // CU count per device, filled on first use (atomic: concurrent callers may
+  // both fill it, with the same value)
+  static std::atomic<int> cu_count[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cu_count[dev] == 0) {
+  int cus = cu_count[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    cu_count[dev] = n > 0 ? n : 1;
+    cus = n > 0 ? n : 1;
+    cu_count[dev].store(cus, std::memory_order_relaxed);
   }
   const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.Nq);
   // as many workgroups as CUs, or one per tile when the tiles do not fill the
   // CUs (the kernel derives the same choice from gridDim)
-  const int grid = tiles <= cu_count[dev] ? (int)tiles : (int)std::min<long long>(units, cu_count[dev]);
+  const int grid = tiles <= cus ? (int)tiles : (int)std::min<long long>(units, cus);
   const dim3 g(grid), blk(kThreads);
   if (d_v != 128) return hipErrorInvalidValue;
   if (d_qk != 128 && d_qk != 192) return hipErrorInvalidValue;

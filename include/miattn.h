@@ -5,8 +5,9 @@
  * frees or synchronises: all work is enqueued on the caller's stream and the
  * calls return as soon as it is enqueued.  Arguments are validated on the host
  * before anything is enqueued, so a call that returns an error has launched
- * nothing.  No C++ exception crosses this interface.  The library keeps no
- * mutable global state; calls are reentrant.
+ * nothing.  No C++ exception crosses this interface.  The only state the
+ * library keeps is a per-device cache of the compute-unit count (atomic);
+ * calls are reentrant and may come from several host threads.
  *
  * Page legend for the citations:
  *   [P1] "Zyphra ZYFA: 1.76x FP8 FlashAttention Speedup on AMD MI355X"
