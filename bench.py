@@ -19,7 +19,10 @@ one per head (``attn_fwd_block64``) is reported under ``block64``.
 ``roofline`` describes the attention kernel (the dominant one): its algorithmic
 FLOPs per launch divided by its average launch duration, measured with HIP
 events on the launch stream inside the timed region, against the dense MFMA
-peak of its dtype.  ``cpu_baseline`` times the CPU oracle (test
+peak of its dtype.  ``sclk_mhz`` is the graphics clock sampled (amdsmi) over
+the second half of 2.5 s of back-to-back launches after the timed region, and
+``frac_at_sclk`` the fraction of the peak scaled from its 2.4 GHz to that clock
+(the random operand data holds the clock below 2.4 GHz).  ``cpu_baseline`` times the CPU oracle (test
 infrastructure, untuned) on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -71,6 +74,58 @@ def measured_traffic(workload: str, launches_bytes: float):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+_AMDSMI = []  # [handle] once amdsmi is initialised, [None] if unavailable
+
+
+def amdsmi_handle():
+    """The first GPU's amdsmi handle (initialised once), or None."""
+    if not _AMDSMI:
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            _AMDSMI.append(amdsmi.amdsmi_get_processor_handles()[0])
+        except Exception:
+            _AMDSMI.append(None)
+    return _AMDSMI[0]
+
+
+def sample_sclk(step, ms_per_launch: float, seconds: float = 2.5):
+    """Mean graphics clock in MHz (amdsmi's current-clock reading, sampled every
+    20 ms) over about `seconds` of back-to-back launches of `step`, run after
+    the timed region; None where amdsmi is unavailable.  Only the second half of
+    the samples counts: the reading is a moving average that lags the load by a
+    good part of a second."""
+    import threading
+
+    import torch
+
+    handle = amdsmi_handle()
+    if handle is None:
+        return None
+    import amdsmi
+
+    n = max(20, int(seconds * 1e3 / max(ms_per_launch, 1e-3)))
+    clocks, stop = [], threading.Event()
+
+    def sample():
+        while not stop.wait(0.02):
+            try:
+                clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+            except Exception:
+                pass
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    clocks = clocks[len(clocks) // 2:]
+    return round(sum(clocks) / len(clocks), 1) if clocks else None
 
 
 def run_gpu(w, steps: int, warmup: int):
@@ -142,7 +197,8 @@ def run_gpu(w, steps: int, warmup: int):
     t1 = time.perf_counter()
     attn_ms = [a.elapsed_time(b) for a, b in events]
     ms_per_step = (t1 - t0) * 1e3 / steps
-    return ms_per_step, attn_ms, front_ms
+    sclk = sample_sclk(step, ms_per_step)
+    return ms_per_step, attn_ms, front_ms, sclk
 
 
 def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
@@ -190,7 +246,10 @@ def run_chunk(w, Nq: int, steps: int, warmup: int):
     return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
 
 
-def roofline(w, attn_ms, flops=None):
+PEAK_SCLK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
+
+
+def roofline(w, attn_ms, flops=None, sclk=None):
     flops = w.causal_flops if flops is None else flops
     avg_s = sum(attn_ms) / len(attn_ms) * 1e-3
     achieved = flops / avg_s / 1e12
@@ -206,6 +265,10 @@ def roofline(w, attn_ms, flops=None):
         "avg_launch_ms": round(avg_s * 1e3, 4),
         "min_launch_ms": round(min(attn_ms), 4),
         "flops_per_launch": flops,
+        # sustained graphics clock over back-to-back launches, and the fraction
+        # of the peak scaled to that clock (the MFMA work per cycle is fixed)
+        "sclk_mhz": sclk,
+        "frac_at_sclk": None if not sclk else round(achieved / (peak * sclk / PEAK_SCLK_MHZ), 4),
     }
 
 
@@ -382,13 +445,14 @@ def main(argv=None):
     if args.clock_study:
         return clock_study(args.study_seconds)
     w = WORKLOADS[args.workload]
+    amdsmi_handle()  # initialised before any launch
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    ms, attn_ms, front_ms = run_gpu(w, args.steps, args.warmup)
+    ms, attn_ms, front_ms, sclk = run_gpu(w, args.steps, args.warmup)
     value = w.causal_flops / (ms * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -409,30 +473,30 @@ def main(argv=None):
             "outlier_channels": w.outliers, "hadamard": w.hadamard,
             "step": "one causal attention launch",
         },
-        "roofline": roofline(w, attn_ms),
+        "roofline": roofline(w, attn_ms, sclk=sclk),
     }
     if front_ms is not None:
         rec["front_end"] = {"what": "quantize Q, K, V (bf16 -> e4m3, per-head amax/448), timed apart from the metric",
                             "ms": round(front_ms, 4)}
     if not args.no_bf16 and w.dtype == "fp8":
         wb = WORKLOADS[args.bf16_workload]
-        msb, attn_b, _ = run_gpu(wb, args.steps, args.warmup)
+        msb, attn_b, _, sclk_b = run_gpu(wb, args.steps, args.warmup)
         rec["bf16"] = {
             "workload": wb.name,
             "value": round(wb.causal_flops / (msb * 1e-3) / 1e12, 1),
             "ms_per_step": round(msb, 4),
-            "roofline": roofline(wb, attn_b),
+            "roofline": roofline(wb, attn_b, sclk=sclk_b),
         }
     if not args.no_block64 and w.name == "fp8_mha_n32k":
         wq = WORKLOADS["fp8_mha_n32k_block64"]
-        msq, attn_q, front_q = run_gpu(wq, args.steps, args.warmup)
+        msq, attn_q, front_q, sclk_q = run_gpu(wq, args.steps, args.warmup)
         rec["block64"] = {
             "workload": f"{wq.name}: the same inputs with one power-of-two scale per 64 positions "
                         "(K and V scales applied by the scaled MFMAs)",
             "value": round(wq.causal_flops / (msq * 1e-3) / 1e12, 1),
             "ms_per_step": round(msq, 4),
             "front_end_ms": round(front_q, 4),
-            "roofline": roofline(wq, attn_q),
+            "roofline": roofline(wq, attn_q, sclk=sclk_q),
         }
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
