@@ -113,8 +113,10 @@ struct Cfg {
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
   static constexpr int LDS_BYTES = 2 * V_TILE + 2 * K_TILE;
   // log2-domain growth of the running max tolerated before rescaling, and the
-  // power-of-two shift applied to FP8 probabilities (p <= 2^(THRESH+SHIFT) <= 256)
-  static constexpr float THRESH = FP8 ? 2.0f : 8.0f;
+  // power-of-two shift applied to FP8 probabilities: p <= 2^(THRESH + SHIFT),
+  // whose lean-P code round(8 (THRESH + SHIFT) + C0) = 126 is e4m3's largest
+  // finite value (448) for THRESH + SHIFT < 8.855
+  static constexpr float THRESH = FP8 ? 2.75f : 8.0f;
   static constexpr float SHIFT = FP8 ? 6.0f : 0.0f;
   // FP8 probabilities are written as e4m3 codes straight from the log2-domain
   // score ("lean P"): the code of 2^x is about 8x + 56, exact at integer x.

@@ -9,7 +9,7 @@ or 6e-2 (FP8), as for the plain path.  LSE (natural log), absolute error:
   error <= 2^-9, so |d lse| <= ln(1 + 2^-9) ~ 2e-3) and the fp32 scores carry
   accumulation error well below that: bound 5e-3.
 * FP8: a probability 2^t (t = x - m + 6, log2 units, with the running
-  reference m within [row max - 2, row max + 1/8]) becomes the e4m3 code
+  reference m within [row max - 2.75, row max + 1/8]) becomes the e4m3 code
   round(8t + 55.66).  For t >= -5.96 (normal codes) its log error lies in
   [-0.0728, +0.0728] (the extremes of ln e4m3(round(8t + 55.66)) - t ln 2);
   below that the subnormal codes only under-represent it, down to zero.  So per
