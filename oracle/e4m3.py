@@ -23,7 +23,15 @@ def e4m3_decode(codes) -> np.ndarray:
 
     value = (-1)^s * 2^(e-7) * (1 + m/8)   for e >= 1
           = (-1)^s * 2^(-6)  * (m/8)       for e == 0 (subnormal)
+
+    The formula is evaluated once for each of the 256 codes and the result
+    indexed by the input (the same values, without evaluating it per element
+    of large tensors).
     """
+    return _decode_formula(np.arange(256, dtype=np.uint8))[np.asarray(codes, dtype=np.uint8)]
+
+
+def _decode_formula(codes) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     s = (c >> 7) & 1
     e = (c >> 3) & 0xF

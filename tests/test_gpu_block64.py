@@ -225,3 +225,32 @@ def test_block64_full_size_sampled_rows(require_gpu):
         ref, _ = attn_chunk_ref_rows(sl(cq, sq, [h]), sl(ck, sk, [h]), sl(cv, sv, [h]), rows=rows)
         got = out[:, rows][:, :, [h]].cpu()
         assert rel_fro(got, ref) <= TOL["fp8"], (h, rel_fro(got, ref))
+
+
+def test_block64_at_the_key_limit(require_gpu):
+    # Nk = 2^20 keys, the largest block-scaled launch (8192 key tiles: every
+    # staged exponent word in use), a ragged chunk of 100 queries at the end
+    # (K and V are drawn as random finite e4m3 codes with random power-of-two
+    # block scales, the kernel's input format; the quantizer is pinned above)
+    B, Nq, Nk, Hq, Hkv, d = 1, 100, 1 << 20, 2, 1, 128
+    rng = np.random.default_rng(77)
+    cq, sq = quantize_block64_ref(rng.standard_normal((B, Nq, Hq, d)).astype(np.float32))
+    nb = Nk // 64
+
+    def codes_and_scales():
+        c = rng.integers(0, 256, size=(B, Nk, Hkv, d), dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x7E  # no NaN codes
+        return c, (np.float32(2.0) ** rng.integers(-12, -4, size=(B, Hkv, nb))).astype(np.float32)
+
+    (ck, sk), (cv, sv) = codes_and_scales(), codes_and_scales()
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
+    out, lse = miattn.attn_fwd_block64(*dev)
+    torch.cuda.synchronize()
+    ref_in = (dequantize_block64_ref(cq, sq), dequantize_block64_ref(ck, sk), dequantize_block64_ref(cv, sv))
+    ref, ref_lse = attn_chunk_ref_rows(*ref_in)
+    assert rel_fro(out.cpu(), ref) <= TOL["fp8"]
+    _check_lse("fp8", lse.cpu().numpy().astype(np.float64), ref_lse, ref_in)
+    with pytest.raises(miattn.MiattnError):  # one key more is refused before any launch
+        kk = torch.zeros(B, Nk + 1, Hkv, d, dtype=torch.uint8, device="cuda")
+        ss = torch.ones(B, Hkv, (Nk + 1 + 63) // 64, device="cuda")
+        miattn.attn_fwd_block64(dev[0], kk, kk, dev[3], ss, ss)
