@@ -230,17 +230,21 @@ def test_block64_full_size_sampled_rows(require_gpu):
 def test_block64_at_the_key_limit(require_gpu):
     # Nk = 2^20 keys, the largest block-scaled launch (8192 key tiles: every
     # staged exponent word in use), a ragged chunk of 100 queries at the end
-    # (K and V are drawn as random finite e4m3 codes with random power-of-two
-    # block scales, the kernel's input format; the quantizer is pinned above)
+    # K and V: N(0, 1) values coded per block with a random exponent e in
+    # {-6, -5, -4} (codes = e4m3(x * 2^-e), torch's round-to-nearest-even
+    # conversion; the library's quantizer is pinned above), so the magnitudes
+    # are uniform while every block's exponent must be applied to read it
     B, Nq, Nk, Hq, Hkv, d = 1, 100, 1 << 20, 2, 1, 128
     rng = np.random.default_rng(77)
     cq, sq = quantize_block64_ref(rng.standard_normal((B, Nq, Hq, d)).astype(np.float32))
     nb = Nk // 64
 
     def codes_and_scales():
-        c = rng.integers(0, 256, size=(B, Nk, Hkv, d), dtype=np.uint8)
-        c[(c & 0x7F) == 0x7F] = 0x7E  # no NaN codes
-        return c, (np.float32(2.0) ** rng.integers(-12, -4, size=(B, Hkv, nb))).astype(np.float32)
+        e = rng.integers(-6, -3, size=(B, Hkv, nb))
+        x = torch.from_numpy(rng.standard_normal((B, Nk, Hkv, d)).astype(np.float32))
+        inv = torch.from_numpy((2.0 ** -np.repeat(e, 64, axis=2)).astype(np.float32)).permute(0, 2, 1)[..., None]
+        c = (x * inv).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        return c, (np.float32(2.0) ** e).astype(np.float32)
 
     (ck, sk), (cv, sv) = codes_and_scales(), codes_and_scales()
     dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
