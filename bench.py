@@ -14,7 +14,8 @@ of a chunked prefill (the last 8192 positions of the same 32K FP8 sequence
 against all 32768 keys, with the LSE output) under ``chunk``, its FLOPs
 counted the same way: B * Hq * (2 Nq Nk - Nq^2) * (d_qk + d_v).  The same FP8
 workload quantized with one power-of-two scale per 64 positions instead of
-one per head (``attn_fwd_block64``) is reported under ``block64``.
+one per head (``attn_fwd_block64``) is reported under ``block64``, and with
+the probabilities scaled per block as well under ``block64.p_block_scale``.
 
 ``roofline`` describes the attention kernel (the dominant one): its algorithmic
 FLOPs per launch divided by its average launch duration, measured with HIP
@@ -179,7 +180,7 @@ def run_gpu(w, steps: int, warmup: int):
         if ev is not None:
             ev[0].record(stream)
         if block64:
-            miattn.attn_fwd_block64(*args, out=out, with_lse=False)
+            miattn.attn_fwd_block64(*args, out=out, with_lse=False, p_block_scale=w.p_block_scale)
         else:
             miattn.attn_fwd(*args, out=out)
         if ev is not None:
@@ -255,7 +256,8 @@ def roofline(w, attn_ms, flops=None, sclk=None):
     achieved = flops / avg_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     return {
-        "kernel": f"attn_fwd_{w.dtype}{'_block64' if w.scales == 'block64' else ''}_kernel<{w.d_qk},{w.d_v}>",
+        "kernel": f"attn_fwd_{w.dtype}{'_block64' if w.scales == 'block64' else ''}"
+                  f"{'_pscale' if w.p_block_scale else ''}_kernel<{w.d_qk},{w.d_v}>",
         "bound": "mfma",
         "achieved": round(achieved, 1),
         "peak": peak,
@@ -497,6 +499,14 @@ def main(argv=None):
             "ms_per_step": round(msq, 4),
             "front_end_ms": round(front_q, 4),
             "roofline": roofline(wq, attn_q, sclk=sclk_q),
+        }
+        wp = WORKLOADS["fp8_mha_n32k_block64_pscale"]
+        msp, attn_p, _, sclk_p = run_gpu(wp, args.steps, args.warmup)
+        rec["block64"]["p_block_scale"] = {
+            "workload": f"{wp.name}: probabilities also scaled per block by powers of two",
+            "value": round(wp.causal_flops / (msp * 1e-3) / 1e12, 1),
+            "ms_per_step": round(msp, 4),
+            "roofline": roofline(wp, attn_p, sclk=sclk_p),
         }
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries

@@ -13,7 +13,8 @@ Entry points (same names as the C ABI):
   lse=None, with_lse=True, softmax_scale=None)``
 * ``attn_quantize_fp8(x, hadamard=False, out=None, scale=None)``
 * ``attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None,
-  with_lse=True, softmax_scale=None)`` (FP8 with per-64-position scales)
+  with_lse=True, softmax_scale=None, p_block_scale=False)`` (FP8 with
+  per-64-position scales, optionally power-of-two scaled probabilities)
 * ``attn_quantize_fp8_block64(x, hadamard=False, out=None, scale=None)``
 * ``attn_status_string(status)``, ``attn_version()``
 
@@ -81,7 +82,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_chunk.restype = ci
     lib.attn_quantize_fp8.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8.restype = ci
-    lib.attn_fwd_block64.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, vp]
+    lib.attn_fwd_block64.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, ci,
+                                     vp]
     lib.attn_fwd_block64.restype = ci
     lib.attn_quantize_fp8_block64.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8_block64.restype = ci
@@ -232,13 +234,17 @@ def _lse_tensor(lse, with_lse, q, B, Hq, Nq):
     return lse
 
 
-def attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, with_lse=True, softmax_scale=None):
+def attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, with_lse=True, softmax_scale=None,
+                     p_block_scale=False):
     """FP8 causal attention with per-64-position scales: q [B,Nq,Hq,d_qk],
     k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] e4m3 codes (uint8 or float8_e4m3fn),
     q_scale fp32 [B,Hq,ceil(Nq/64)], k_scale and v_scale fp32
     [B,Hkv,ceil(Nk/64)] (powers of two, as ``attn_quantize_fp8_block64``
-    writes them).  Query row i sees keys j <= i + Nk - Nq.  Returns
-    ``(out, lse)`` as ``attn_fwd_chunk``."""
+    writes them).  Query row i sees keys j <= i + Nk - Nq.  ``p_block_scale``
+    shifts each query's probabilities of every 64-key step by a power of two
+    of their own before rounding (undone by the scaled MFMAs), which keeps key
+    blocks far below the row max at e4m3 precision.  Returns ``(out, lse)`` as
+    ``attn_fwd_chunk``."""
     torch = _torch()
     if q.dtype == torch.bfloat16:
         raise TypeError("attn_fwd_block64 takes e4m3 codes (quantize with attn_quantize_fp8_block64)")
@@ -248,7 +254,8 @@ def attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, wit
     st = load_library().attn_fwd_block64(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
         B, Hq, Hkv, Nq, Nk, dqk, dv, ptr_s[0], ptr_s[1], ptr_s[2],
-        0.0 if softmax_scale is None else float(softmax_scale), _stream_handle(q.device),
+        0.0 if softmax_scale is None else float(softmax_scale), 1 if p_block_scale else 0,
+        _stream_handle(q.device),
     )
     if st != 0:
         raise MiattnError("attn_fwd_block64", st)
@@ -295,14 +302,16 @@ def attn_quantize_fp8_block64(x, hadamard: bool = False, out=None, scale=None):
 
 
 def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, return_lse=False, fp8=False,
-                    hadamard=False, fp8_scales="head"):
+                    hadamard=False, fp8_scales="head", p_block_scale=False):
     """Drop-in for the ``flash_attn_func`` call convention: q [B,Nq,Hq,d_qk],
     k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] BF16 GPU tensors (BSHD), causal, with
     Nq <= Nk (the queries are the last Nq positions; Nq == Nk is a plain
     prefill).  ``fp8=True`` quantizes q, k, v to e4m3 with the library's
     quantizer -- one scale per (batch, head) (``fp8_scales="head"``) or one
     power-of-two scale per 64 positions (``fp8_scales="block64"``);
-    ``hadamard=True`` rotates q and k first -- and runs the FP8 path.  Returns
+    ``hadamard=True`` rotates q and k first -- and runs the FP8 path;
+    ``p_block_scale=True`` (with ``fp8_scales="block64"``) also scales the
+    probabilities per block by powers of two.  Returns
     the bf16 output, or ``(out, lse)`` with ``return_lse`` (lse fp32
     [B,Hq,Nq], natural log).  Only what the kernels compute is accepted:
     causal=False and dropout raise."""
@@ -318,11 +327,14 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, ret
         raise ValueError("hadamard applies to the FP8 path only")
     if fp8_scales not in ("head", "block64"):
         raise ValueError('fp8_scales must be "head" or "block64"')
+    if p_block_scale and not (fp8 and fp8_scales == "block64"):
+        raise ValueError('p_block_scale needs fp8=True and fp8_scales="block64"')
     if fp8 and fp8_scales == "block64":
         (cq, sq) = attn_quantize_fp8_block64(q.contiguous(), hadamard=hadamard)
         (ck, sk) = attn_quantize_fp8_block64(k.contiguous(), hadamard=hadamard)
         (cv, sv) = attn_quantize_fp8_block64(v.contiguous())
-        out, lse = attn_fwd_block64(cq, ck, cv, sq, sk, sv, with_lse=return_lse, softmax_scale=softmax_scale)
+        out, lse = attn_fwd_block64(cq, ck, cv, sq, sk, sv, with_lse=return_lse, softmax_scale=softmax_scale,
+                                    p_block_scale=p_block_scale)
         return (out, lse) if return_lse else out
     if fp8:
         (cq, sq) = attn_quantize_fp8(q.contiguous(), hadamard=hadamard)

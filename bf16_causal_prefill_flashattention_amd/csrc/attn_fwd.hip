@@ -61,6 +61,17 @@
 // P.V k-step each lie in one 64-key block), at no vector cost.  The exponents of
 // a work item's key tiles are staged in LDS, one word per 128-key tile.
 //
+// Optional probability block scaling (with block scales, FP8): the lean-P
+// codes have about 13 octaves of range below the running max, so key blocks
+// whose scores lie far below it round to zero.  With it, a query's 64
+// probabilities of a P.V k-step are shifted up by k octaves, k = floor(running
+// max - their max), and the P.V and row-sum MFMAs scale them back by the E8M0
+// exponent 2^-k ([P3] "ZYFA 如何工作？": per-64-key power-of-two scaling of P
+// undone by the scaled MFMA).  The scaled MFMAs read the exponent of a 32-key
+// block of column j from lane j + 32 b, while each lane holds half of both
+// blocks of its k-step, so both lanes of a query take the k-step's max across
+// the pair (one exponent per query and 64 keys).
+//
 // Probabilities.  The running max is only raised when a tile's max exceeds it
 // by more than a small threshold, so most tiles skip the rescale of the output
 // accumulator.  The row sum is taken from the rounded probabilities that feed
@@ -258,6 +269,7 @@ struct RowState {
   f32x16 o[DV / 32];  // O^T accumulator: lane owns query l % 32, channels 32d + 8i + 4hl + j
   float m;            // running max, log2 domain
   f32x4 l4;           // the full row sum (every entry)
+  f32x16 l16;         // the same, from the all-ones row-sum MFMA (probability block scaling)
   float kc;           // lean P: integer code offset K = 8 (SHIFT - m) + C0 (m kept on that grid)
 };
 
@@ -300,6 +312,7 @@ struct Wave {
   typename QOp<FP8>::T q[C::QK_STEPS];
   f32x16 s[NBLK];
   uint32_t pk[FP8 ? C::BN / 8 : C::BN / 4];  // this lane's probabilities of the tile (half its keys), MFMA B-operand order
+  uint32_t pscale;  // probability block scaling: E8M0 exponent of this query's P for k-step ks in byte ks
   RowState<DV> st;
 };
 
@@ -311,7 +324,7 @@ struct Wave {
 // key order; the order only decides which tiles the workgroups of an XCD read
 // at the same time).  Called by every thread of the workgroup; leaves no load
 // in flight and no wave reading LDS when it returns.
-template <int DQK, int DV, bool FP8, bool BS>
+template <int DQK, int DV, bool FP8, bool BS, bool PS>
 __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
                                           bool rev) {
   using C = Cfg<FP8, DQK, DV>;
@@ -462,6 +475,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   for (int d = 0; d < DV / 32; ++d) wv.st.o[d] = zero16();
   wv.st.m = -1e30f;
   wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (PS) wv.st.l16 = zero16();
   wv.st.kc = 0.f;
   // Row-sum selector (A operand of the 16x16 row-sum MFMA): 1.0 where the lane
   // group's parity matches its row group's parity, else 0.  Lane l then finds
@@ -470,6 +484,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   const bool sel_on = ((lane >> 4) & 1) == (((lane & 15) >> 2) & 1);
   const int sel_w = sel_on ? (FP8 ? 0x38383838 : 0x3f803f80) : 0;  // e4m3 / bf16 ones
   const i32x8 sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
+  // With probability block scaling the row sum is a 32x32x64 MFMA against an
+  // all-ones A: its B exponents are read per (column, 32-key block) as in the
+  // P.V product (the 16x16x128 form reads one column's exponents from the lanes
+  // of a single query, but that column also holds another query's keys).
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
   // E8M0 exponents of the K tile (bytes 0, 1: its two 64-key blocks) and V tile
   // (bytes 2, 3) of the current matrix phase (block scales only)
@@ -523,12 +543,20 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
         const i32x8 pb = {(int)wv.pk[8 * ks + 0], (int)wv.pk[8 * ks + 1], (int)wv.pk[8 * ks + 2],
                           (int)wv.pk[8 * ks + 3], (int)wv.pk[8 * ks + 4], (int)wv.pk[8 * ks + 5],
                           (int)wv.pk[8 * ks + 6], (int)wv.pk[8 * ks + 7]};
-        if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
-        if constexpr (BS)
-          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
-                                : mfma_fp8_32x32x64_sa<3>(a, pb, wv.st.o[db], (int)vexp);
-        else
-          wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
+        if constexpr (PS) {
+          if (db == 0)
+            wv.st.l16 = ks == 0 ? mfma_fp8_32x32x64_sab<0, 0>(ones, pb, wv.st.l16, 127, (int)wv.pscale)
+                                : mfma_fp8_32x32x64_sab<0, 1>(ones, pb, wv.st.l16, 127, (int)wv.pscale);
+          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
+                                : mfma_fp8_32x32x64_sab<3, 1>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
+        } else {
+          if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
+          if constexpr (BS)
+            wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
+                                  : mfma_fp8_32x32x64_sa<3>(a, pb, wv.st.o[db], (int)vexp);
+          else
+            wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
+        }
       } else {
         const int chunk = i / (DV / 32), db = i % (DV / 32);
         const i32x4 pw = {(int)wv.pk[4 * chunk], (int)wv.pk[4 * chunk + 1], (int)wv.pk[4 * chunk + 2],
@@ -609,13 +637,15 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
           wv.s[blk][r] = __uint_as_float((hide & 0xff800000u) | (~hide & __float_as_uint(x)));
         }
     }
-    // row max: four independent chains of 3-input max (two new values each)
+    // row max: four independent chains of 3-input max (two new values each);
+    // with probability block scaling, chains 2ks and 2ks+1 cover exactly this
+    // lane's keys of k-step ks (blocks 2ks, 2ks+1)
     float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float& m = mc[(blk * 8 + r / 2) & 3];
+        float& m = mc[PS ? 2 * (blk >> 1) + ((r >> 1) & 1) : (blk * 8 + r / 2) & 3];
         m = fmaxf(fmaxf(m, wv.s[blk][r]), wv.s[blk][r + 1]);
       }
     float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
@@ -633,19 +663,40 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
       const float alpha = fast_exp2(wv.st.m - m_new);
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d) wv.st.o[d] *= alpha;
-      wv.st.l4 *= alpha;
+      if constexpr (PS)
+        wv.st.l16 *= alpha;
+      else
+        wv.st.l4 *= alpha;
       wv.st.m = m_new;
     }
     const float bias = C::SHIFT - wv.st.m;
     if constexpr (C::LEAN_P) {
       // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
       const float c8 = 8.f * c, b8 = kLeanMagic + wv.st.kc, magic = kLeanMagic;
+      float bks[NBLK / 2];  // code offset of k-step ks
+      if constexpr (PS) {
+        // k = floor(running max - the query's max over the 64 keys of k-step
+        // ks) octaves, in [0, 126]: the codes move up by 8k, the MFMA scale is
+        // 2^-k (a k-step whose keys are all masked gets k = 126 and codes 0)
+        uint32_t ps = 0;
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) {
+          const float bmax = lane_xor32_max(fmaxf(mc[2 * ks], mc[2 * ks + 1]));
+          const float k = fminf(fmaxf(floorf(__builtin_fmaf(-bmax, c, wv.st.m)), 0.f), 126.f);
+          bks[ks] = __builtin_fmaf(8.f, k, b8);
+          ps |= (uint32_t)(127 - (int)k) << (8 * ks);
+        }
+        wv.pscale = ps;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) bks[ks] = b8;
+      }
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           wv.pk[4 * blk + i] = lean_p4(wv.s[blk][4 * i], wv.s[blk][4 * i + 1], wv.s[blk][4 * i + 2],
-                                       wv.s[blk][4 * i + 3], c8, b8, magic);
+                                       wv.s[blk][4 * i + 3], c8, bks[blk >> 1], magic);
     } else if constexpr (FP8) {
       // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
 #pragma unroll
@@ -694,6 +745,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     lds_store16(Vs + C::V_TILE + 16 * (tid + kThreads * i), i32x4{0, 0, 0, 0});
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(wv.pk) / sizeof(wv.pk[0])); ++i) wv.pk[i] = 0u;
+  wv.pscale = 0x7f7f7f7fu;  // unit scales
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (grp == 1) {
     issue_step(0);
@@ -735,12 +787,13 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   if (grp == 0) barrier(false);
 
   // ---- epilogue: normalise by the row sum and store BF16
-  const float inv = sv / wv.st.l4[0];
+  const float lsum = PS ? wv.st.l16[0] : wv.st.l4[0];
+  const float inv = sv / lsum;
   if (my_q < Nq) {
     // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
     // log2 sum_j 2^x_j = m - SHIFT + log2(l); lanes l and l + 32 share a query
     if (p.lse != nullptr && hl == 0)
-      p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(wv.st.l4[0])) * 0.69314718055994531f;
+      p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(lsum)) * 0.69314718055994531f;
     __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * Nq + my_q) * p.Hq + h) * DV;
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) {
@@ -770,7 +823,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
 // tiles instead of one stream each.
-template <int DQK, int DV, bool FP8, bool BS>
+template <int DQK, int DV, bool FP8, bool BS, bool PS>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
@@ -790,7 +843,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
     const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
     const int j = u % per_bh;
     const int qt = half == 0 ? nqt - 1 - j : j;
-    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8, BS>(p, smem, ebuf, bh, qt, !single && half == 1);
+    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8, BS, PS>(p, smem, ebuf, bh, qt, !single && half == 1);
     if (single) {
       u += nrank;
     } else {
@@ -835,23 +888,31 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
   const dim3 g(grid), blk(kThreads);
   if (d_v != 128) return hipErrorInvalidValue;
   if (d_qk != 128 && d_qk != 192) return hipErrorInvalidValue;
+  if (p.p_block_scale && !p.block64) return hipErrorInvalidValue;
   if (dtype == 0) {
     if (p.block64) return hipErrorInvalidValue;
     if (d_qk == 128)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, false, false>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, false, false, false>), g, blk, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, false, false>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, false, false, false>), g, blk, 0, stream, p);
   } else if (p.block64) {
     if (p.Nk > kBlock64MaxKeys) return hipErrorInvalidValue;
-    if (d_qk == 128)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, true>), g, blk, 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, true>), g, blk, 0, stream, p);
+    if (p.p_block_scale) {
+      if (d_qk == 128)
+        hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, true, true>), g, blk, 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, true, true>), g, blk, 0, stream, p);
+    } else {
+      if (d_qk == 128)
+        hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, true, false>), g, blk, 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, true, false>), g, blk, 0, stream, p);
+    }
   } else {
     if (d_qk == 128)
-      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, false>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<128, 128, true, false, false>), g, blk, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, false>), g, blk, 0, stream, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<192, 128, true, false, false>), g, blk, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -49,12 +49,27 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64_sa(i32x8 a, i32x8 b, f32x16 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, scale_a, 0, 127);
 }
 
+// As mfma_fp8_32x32x64 with A scaled by byte SELA of scale_a and B by byte SELB
+// of scale_b (E8M0 exponents).  B's scale is per lane: lane l's byte scales the
+// 32 k-slots of column l % 32 it supplies.
+template <int SELA, int SELB>
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64_sab(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SELA, scale_a, SELB, scale_b);
+}
+
 // D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), unit block scales.  Lane l
 // supplies 32 k-slots of A row / B column (l % 16); lane group l / 16 selects
 // which quarter of the 128 k-slots.  D: lane l holds column (l % 16), rows
 // 4*(l / 16) + j in register j.
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// As mfma_fp8_16x16x128 with B scaled per lane by byte SELB of scale_b (E8M0):
+// lane l's byte scales the 32 k-slots it supplies.
+template <int SELB>
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128_sb(i32x8 a, i32x8 b, f32x4 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, SELB, scale_b);
 }
 
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies 8 k-slots of

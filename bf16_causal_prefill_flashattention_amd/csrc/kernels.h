@@ -26,6 +26,10 @@ struct AttnParams {
   int B, Hq, Hkv, Nq, Nk;
   float sm_scale_log2;  // softmax scale times log2(e)
   int block64;
+  // with block64: each lane's 32 probabilities of a 64-key k-step are shifted by
+  // a power of two of their own (the octaves their max lies below the running
+  // max) and the scaled MFMAs undo it
+  int p_block_scale;
 };
 
 // Largest key count of a block-scaled launch: the exponents of all key tiles of

@@ -43,7 +43,8 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, co
 
 int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                  int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
-                 const float* v_scale, double tau, void* stream, bool block64 = false) {
+                 const float* v_scale, double tau, void* stream, bool block64 = false,
+                 bool p_block_scale = false) {
   miattn::AttnParams p;
   p.q = q;
   p.k = k;
@@ -60,6 +61,7 @@ int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.Nk = Nk;
   p.sm_scale_log2 = (float)(1.4426950408889634 * tau);  // log2-domain softmax scale
   p.block64 = block64 ? 1 : 0;
+  p.p_block_scale = p_block_scale ? 1 : 0;
   const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
@@ -134,7 +136,8 @@ int attn_quantize_fp8(const void* x, int x_dtype, void* x_fp8, float* scale, int
 
 int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                      int Nq, int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale,
-                     const float* v_scale, float softmax_scale, void* stream) {
+                     const float* v_scale, float softmax_scale, int p_block_scale, void* stream) {
+  if (p_block_scale != 0 && p_block_scale != 1) return MIATTN_ERR_DTYPE;
   if (!(softmax_scale == 0.0f || (std::isfinite(softmax_scale) && softmax_scale > 0.0f))) return MIATTN_ERR_VALUE;
   const int st = validate_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale,
                                    k_scale, v_scale);
@@ -143,7 +146,7 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
   if (B == 0 || Nq == 0) return MIATTN_OK;
   const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
   return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale, k_scale,
-                      v_scale, tau, stream, true);
+                      v_scale, tau, stream, true, p_block_scale != 0);
 }
 
 int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,

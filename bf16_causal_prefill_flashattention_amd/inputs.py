@@ -24,7 +24,9 @@ Recipe (one torch CPU generator per tensor, fp32 N(0, 1)):
   rows of all heads (magnitudes that drift along the sequence, the case finer
   FP8 scale granularity is for).
   ``scales`` names the FP8 scale granularity a workload is quantized with:
-  "head" (one scale per batch and head) or "block64" (one per 64 positions).
+  "head" (one scale per batch and head) or "block64" (one per 64 positions);
+  ``p_block_scale`` asks the block-scaled attention to scale its probabilities
+  per block by powers of two as well.
 """
 
 from __future__ import annotations
@@ -50,6 +52,7 @@ class Workload:
     seed: int = 0
     kv_decades: float = 0.0
     scales: str = "head"
+    p_block_scale: bool = False
     note: str = field(default="", compare=False)
 
     @property
@@ -86,6 +89,9 @@ WORKLOADS = {
     "fp8_mla_n32k": _w("fp8_mla_n32k", "fp8", 1, 16, 16, 32768, 192, 128),
     "fp8_mha_n32k_block64": _w("fp8_mha_n32k_block64", "fp8", 1, 32, 32, 32768, 128, 128, scales="block64",
                                note="the FP8 headline shape with per-64-position scales"),
+    "fp8_mha_n32k_block64_pscale": _w("fp8_mha_n32k_block64_pscale", "fp8", 1, 32, 32, 32768, 128, 128,
+                                      scales="block64", p_block_scale=True,
+                                      note="as fp8_mha_n32k_block64, probabilities scaled per block too"),
 }
 
 

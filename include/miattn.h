@@ -21,7 +21,7 @@
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 3
+#define MIATTN_ABI_VERSION 4
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -188,6 +188,15 @@ int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* sc
  * Query row i sits at position i + Nk - Nq and attends to keys
  * j <= i + Nk - Nq; softmax_scale: tau, 0 selects 1 / sqrt(d_qk), otherwise
  * finite and positive (else MIATTN_ERR_VALUE).
+ * p_block_scale = 1 also scales the probabilities by powers of two: each
+ * query's 64 probabilities of a 64-key P.V step are shifted up by k octaves,
+ * k = floor(running max - their max) in [0, 126], before
+ * rounding to e4m3, and the scaled MFMAs multiply them by 2^-k ([P3] "ZYFA
+ * 如何工作？": per-block power-of-two scaling of P undone by the scaled MFMA).
+ * It keeps key blocks whose scores lie far below the row max (more than about
+ * 13 octaves, where unshifted probabilities round to zero) at e4m3 precision,
+ * at the cost of some vector work per step; p_block_scale = 0 rounds every
+ * probability against the running max.  Any other value: MIATTN_ERR_DTYPE.
  * Sizes: B >= 0, 0 <= Nq <= Nk <= 2^20 (the exponents of a query tile's keys
  * are staged on chip), Hq >= 1, Hkv >= 1, Hq % Hkv == 0, (d_qk, d_v) in
  * {(128, 128), (192, 128)}; B == 0 or Nq == 0 is an empty call.  Alignment,
@@ -195,7 +204,7 @@ int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* sc
  * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
 int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                      int Nq, int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale,
-                     const float* v_scale, float softmax_scale, void* stream);
+                     const float* v_scale, float softmax_scale, int p_block_scale, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -119,8 +119,8 @@ def test_quantize_block64_empty_sequence(lib):
 
 
 def block64(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=128, dv=128, qs=P, ks=P, vs=P,
-            tau=0.0):
-    return lib.attn_fwd_block64(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, qs, ks, vs, tau, None)
+            tau=0.0, pbs=0):
+    return lib.attn_fwd_block64(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, qs, ks, vs, tau, pbs, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -130,8 +130,9 @@ def block64(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=1
     (dict(Nq=8, Nk=(1 << 20) + 1), E_SIZE),
     (dict(dqk=64), E_SHAPE), (dict(dqk=192, dv=192), E_SHAPE),
     (dict(lse=P + 2), E_ALIGN), (dict(ks=P + 2), E_ALIGN), (dict(k=P + 4), E_ALIGN),
-    (dict(tau=-0.5), E_VALUE), (dict(tau=float("nan")), E_VALUE),
+    (dict(tau=-0.5), E_VALUE), (dict(tau=float("nan")), E_VALUE), (dict(pbs=2), E_DTYPE), (dict(pbs=-1), E_DTYPE),
     (dict(Nq=0), OK), (dict(B=0), OK), (dict(Nq=0, q=None, k=None, v=None, o=None), OK),
+    (dict(Nq=0, pbs=1), OK),
 ])
 def test_attn_fwd_block64_validation(lib, kw, expect):
     assert block64(lib, **kw) == expect
@@ -171,5 +172,7 @@ def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
         pkg.flash_attn_func(q, q, q, hadamard=True)
     with pytest.raises(ValueError):
         pkg.flash_attn_func(q, q, q, fp8=True, fp8_scales="tensor")
+    with pytest.raises(ValueError):
+        pkg.flash_attn_func(q, q, q, fp8=True, p_block_scale=True)
     with pytest.raises(ValueError):  # CPU tensors
         pkg.flash_attn_func(q, q, q)

@@ -11,6 +11,11 @@ dimension 192, against the oracle.
 * With every block scale of a (batch, head) equal to one power of two, the
   block-scaled kernel must reproduce the per-head kernel bit for bit: a
   power-of-two scale applied inside the MFMA commutes with every rounding.
+* Probability block scaling (``p_block_scale``): the same parity cases, and on
+  keys whose block magnitudes differ by 2^+-1 it must cut the error of
+  rounding every probability against the running max by at least 1.5x (a CPU
+  emulation of the two roundings against the exact row max on that input:
+  15.9% against 2.3%).
 """
 
 import numpy as np
@@ -121,10 +126,11 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("pbs", [False, True])
 @pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,dqk,outl,dec,had", CASES)
-def test_block64_attention_matches_oracle(require_gpu, B, Nq, Nk, Hq, Hkv, dqk, outl, dec, had):
+def test_block64_attention_matches_oracle(require_gpu, B, Nq, Nk, Hq, Hkv, dqk, outl, dec, had, pbs):
     _, dev, ref_in = _inputs(B, Nq, Nk, Hq, Hkv, dqk, outl, dec, had, seed=Nq + 3 * Nk + Hq)
-    out, lse = miattn.attn_fwd_block64(*dev)
+    out, lse = miattn.attn_fwd_block64(*dev, p_block_scale=pbs)
     torch.cuda.synchronize()
     ref, ref_lse = attn_chunk_ref_rows(*ref_in)
     err = rel_fro(out.cpu(), ref)
@@ -178,7 +184,8 @@ def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk)
     assert torch.equal(lse_h.view(torch.int32), lse_b.view(torch.int32))
 
 
-def test_block64_deterministic_and_writes_only_its_outputs(require_gpu):
+@pytest.mark.parametrize("pbs", [False, True])
+def test_block64_deterministic_and_writes_only_its_outputs(require_gpu, pbs):
     _, dev, _ = _inputs(1, 1000, 1000, 8, 2, 128, 4, 3.0, False, seed=5)
     B, Nq, Hq = 1, 1000, 8
     guard = 4096
@@ -186,10 +193,10 @@ def test_block64_deterministic_and_writes_only_its_outputs(require_gpu):
     lbuf = torch.full((2 * guard + B * Hq * Nq,), -7.0, dtype=torch.float32, device="cuda")
     out = obuf[guard:guard + B * Nq * Hq * 128].view(B, Nq, Hq, 128)
     lse = lbuf[guard:guard + B * Hq * Nq].view(B, Hq, Nq)
-    miattn.attn_fwd_block64(*dev, out=out, lse=lse)
+    miattn.attn_fwd_block64(*dev, out=out, lse=lse, p_block_scale=pbs)
     first_o, first_l = out.clone(), lse.clone()
     for _ in range(20):
-        miattn.attn_fwd_block64(*dev, out=out, lse=lse)
+        miattn.attn_fwd_block64(*dev, out=out, lse=lse, p_block_scale=pbs)
         assert torch.equal(out.view(torch.int16), first_o.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), first_l.view(torch.int32))
     torch.cuda.synchronize()
@@ -227,7 +234,8 @@ def test_block64_full_size_sampled_rows(require_gpu):
         assert rel_fro(got, ref) <= TOL["fp8"], (h, rel_fro(got, ref))
 
 
-def test_block64_at_the_key_limit(require_gpu):
+@pytest.mark.parametrize("pbs", [False, True])
+def test_block64_at_the_key_limit(require_gpu, pbs):
     # Nk = 2^20 keys, the largest block-scaled launch (8192 key tiles: every
     # staged exponent word in use), a ragged chunk of 100 queries at the end
     # K and V: N(0, 1) values coded per block with a random exponent e in
@@ -248,7 +256,7 @@ def test_block64_at_the_key_limit(require_gpu):
 
     (ck, sk), (cv, sv) = codes_and_scales(), codes_and_scales()
     dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
-    out, lse = miattn.attn_fwd_block64(*dev)
+    out, lse = miattn.attn_fwd_block64(*dev, p_block_scale=pbs)
     torch.cuda.synchronize()
     ref_in = (dequantize_block64_ref(cq, sq), dequantize_block64_ref(ck, sk), dequantize_block64_ref(cv, sv))
     ref, ref_lse = attn_chunk_ref_rows(*ref_in)
@@ -258,3 +266,34 @@ def test_block64_at_the_key_limit(require_gpu):
         kk = torch.zeros(B, Nk + 1, Hkv, d, dtype=torch.uint8, device="cuda")
         ss = torch.ones(B, Hkv, (Nk + 1 + 63) // 64, device="cuda")
         miattn.attn_fwd_block64(dev[0], kk, kk, dev[3], ss, ss)
+
+
+def test_p_block_scaling_keeps_far_key_blocks(require_gpu):
+    # K and V blocks of 64 positions scaled by 2^r, r uniform in {-1, 0, 1}:
+    # many keys of the low blocks score more than 13 octaves below the row max,
+    # where probabilities rounded against the row max become zero; shifted per
+    # lane and undone by the scaled MFMAs they keep e4m3 precision
+    B, Nq, Nk, Hq, Hkv, d = 1, 256, 65536, 2, 1, 128
+    rng = np.random.default_rng(5)
+    cq, sq = quantize_block64_ref(rng.standard_normal((B, Nq, Hq, d)).astype(np.float32))
+    nb = Nk // 64
+
+    def codes_and_scales():
+        r = rng.integers(-1, 2, size=(B, Hkv, nb))
+        x = torch.from_numpy(rng.standard_normal((B, Nk, Hkv, d)).astype(np.float32))
+        c = (x * 64.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()  # value = code * 2^(r - 6) = x * 2^r
+        return c, (np.float32(2.0) ** (r - 6)).astype(np.float32)
+
+    (ck, sk), (cv, sv) = codes_and_scales(), codes_and_scales()
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
+    out_s, lse_s = miattn.attn_fwd_block64(*dev, p_block_scale=True)
+    out_0, _ = miattn.attn_fwd_block64(*dev, p_block_scale=False)
+    torch.cuda.synchronize()
+    ref_in = (dequantize_block64_ref(cq, sq), dequantize_block64_ref(ck, sk), dequantize_block64_ref(cv, sv))
+    ref, ref_lse = attn_chunk_ref_rows(*ref_in)
+    e_s, e_0 = rel_fro(out_s.cpu(), ref), rel_fro(out_0.cpu(), ref)
+    # (MI355X: 3.0% against 6.3%; the lazy running max sits up to 2.75 octaves
+    # below the row max, which already lifts part of the tail, so the kernel
+    # without block scaling does better than rounding against the exact max)
+    assert e_s <= TOL["fp8"] and e_0 > 1.5 * e_s, (e_s, e_0)
+    _check_lse("fp8", lse_s.cpu().numpy().astype(np.float64), ref_lse, ref_in)
