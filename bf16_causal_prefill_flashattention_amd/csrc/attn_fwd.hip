@@ -29,11 +29,14 @@
 // accumulator straight into the MFMA B operand, in an order of keys that the
 // V^T operand reproduces when it is read from LDS.
 //
-// Two-group ping-pong.  The matrix core and the vector ALU of a SIMD only run
-// at the same time for instructions of different waves: a wave's own softmax
-// work does not overlap its own matrix instructions.  So the 8 waves form two
-// groups (waves 0-3 and 4-7, one wave of each per SIMD) that run the same loop
-// one phase apart, separated by workgroup barriers:
+// Two-group ping-pong.  A tile's softmax depends on that tile's S = K Q^T
+// MFMAs, and its P.V product on the softmax, so within one wave the two kinds
+// of work of a tile follow each other.  (Independent vector instructions do
+// issue while the wave's own MFMAs execute: on gfx950, 128 independent FMAs
+// interleaved with 16 FP8 32x32x64 MFMAs took the MFMAs' 980 cycles.)  Here the
+// 8 waves form two groups (waves 0-3 and 4-7, one wave of each per SIMD) that
+// run the same loop one phase apart, separated by workgroup barriers, so one
+// wave's softmax runs beside the other's matrix work:
 //   phase 2p   : group A matrix work  | group B vector work
 //   phase 2p+1 : group A vector work  | group B matrix work
 // where "matrix work" of step p is P_{p-1} V_{p-1} followed by S_p = K_p Q^T,
