@@ -56,11 +56,21 @@ PAGES_FP8_HD128_32K = 2672.0  # TFLOP/s, FP8 causal fwd, hd128, N=32K, Gaussian,
 ATTN_KERNEL_SOURCES = ["attn_fwd.hip", "device_common.hpp"]
 
 
-def kernel_source_hash() -> str:
+def code_tokens(text: str) -> str:
+    """Source text without // comments and with whitespace collapsed: what the
+    compiler sees, so editing a comment does not invalidate a profile."""
+    import re
+
+    return " ".join(re.sub(r"//[^\n]*", " ", text).split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the attention kernel's code (comments and layout excluded)."""
     h = hashlib.sha256()
     for s in ATTN_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bf16_causal_prefill_flashattention_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        path = os.path.join(ROOT, "bf16_causal_prefill_flashattention_amd", "csrc", s)
+        text = read(s) if read else open(path, encoding="utf-8").read()
+        h.update(code_tokens(text).encode())
     return h.hexdigest()[:16]
 
 
