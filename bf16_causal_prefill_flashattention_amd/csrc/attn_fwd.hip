@@ -330,6 +330,8 @@ struct Wave {
 template <int DQK, int DV, bool FP8, bool BS, bool PS>
 __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
                                           bool rev) {
+  static_assert(!BS || FP8, "block scales are an FP8 feature");
+  static_assert(!PS || BS, "probability block scaling runs in the block-scaled FP8 kernel");
   using C = Cfg<FP8, DQK, DV>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
