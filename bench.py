@@ -444,7 +444,7 @@ def main(argv=None):
                          "this many bytes: the reference kernel of known traffic for scaling HBM counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the path is a single-GPU kernel and this build has no "
+        print("bench.py measures one GPU only: the path is a single-GPU kernel and the library has no "
               "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
         return 2
 

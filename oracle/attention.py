@@ -8,7 +8,7 @@ prefill attention deserves dedicated optimization"), so the oracle is that plain
 result.  The pages measure error against fp64 attention ([P3] "ZYFA 的 FP8
 注意力有多准确？"), so everything here runs in fp64.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * causal alignment: equal query and key lengths; key j is visible to query i
   iff j <= i;

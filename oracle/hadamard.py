@@ -3,7 +3,7 @@
 The pages (legend in ``oracle/__init__.py``) report that rotating Q and K by a
 Hadamard matrix before FP8 quantization roughly halves the input-quantization
 error at a small time cost ([P3] "ZYFA 的 FP8 注意力有多准确？", [P2] "Accuracy and
-Code").  They do not say which Hadamard matrix; the reading taken (DESIGN.md) is
+Code").  They do not say which Hadamard matrix; the reading taken is
 the plain Sylvester matrix H_128 with no random signs, applied as x <- x H_128,
 with the 1/sqrt(128) normalisation folded into the per-head scale instead of
 into the values.

@@ -5,7 +5,7 @@ per-tensor or per-head scale factors to bring values into the representable
 range, and that finer scaling granularity is one of the places where accuracy
 is won, with FP32 accumulation ([P1] "ZYFA's performance and accuracy data").
 Two granularities are defined here; the steps and their fp32 rounding are
-readings where the pages are silent.
+readings taken where the pages are silent.
 
 Per (batch, head), ``quantize_ref`` (the workloads' amax/448 scales):
 
