@@ -6,7 +6,7 @@ data").  Read as an unsigned integer, the code of a positive value grows by 8
 each time the value doubles ([P3] "ZYFA 如何工作？", the lean-P paragraph).  The
 pages say only "e4m3"; the workloads scale by amax/448, which fixes the OCP
 "e4m3fn" variant: exponent bias 7, largest finite value 448 (code 0x7E), no
-infinities, S.1111.111 is NaN (a reading: the pages say only "e4m3").
+infinities, S.1111.111 is NaN.
 
 Nothing here shares code with the HIP path.
 """
