@@ -768,6 +768,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   // for a few hundred cycles, so they go where the wave has slack).  Group B
   // issues at the end of its vector work.  Every load of step p is waited for
   // at the barrier that ends phase 2p+1, when all waves have issued theirs.
+  // No step runs past T, so no loads are issued for one either: an item ends
+  // with no load in flight that could land in the next item's first tiles.
   auto step = [&](int ps, auto parity, auto group) __attribute__((always_inline)) {
     constexpr bool GA = decltype(group)::value == 0;
     if (GA && FP8) issue_step(ps);
@@ -775,7 +777,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     barrier(!GA);
     if (GA && !FP8) issue_step(ps);
     vector_work(ps);
-    if (!GA) issue_step(ps + 1);
+    if (!GA && ps + 1 <= T) issue_step(ps + 1);
     barrier(GA);
   };
   // one loop per group, so the group decisions inside a step are compile-time
