@@ -386,12 +386,13 @@ def clock_study(seconds: float):
             e1.record()
             torch.cuda.synchronize()
             n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
-            clocks, stop = [], threading.Event()
+            clocks, energy, stop = [], [], threading.Event()
 
             def sample():
                 while not stop.wait(0.05):
                     try:
                         clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+                        energy.append((time.perf_counter(), energy_j()))
                     except Exception:
                         pass
 
@@ -412,8 +413,16 @@ def clock_study(seconds: float):
                 t1, ej1 = time.perf_counter(), energy_j()
                 stop.set()
                 th.join()
+                # The energy counter advances in coarse steps (about once a second on
+                # MI355X boards): the rate between its first and last change inside
+                # the window is the board power; the clock reading lags the load, so
+                # only its second half is kept.
                 watts = (ej1 - ej0) / (t1 - t0)
-                clocks = clocks[len(clocks) // 2:]  # the reading is a moving average that lags the load
+                steps = [energy[i] for i in range(1, len(energy)) if energy[i][1] != energy[i - 1][1]]
+                rec["energy_steps"] = len(steps)
+                if len(steps) >= 2 and steps[-1][0] > steps[0][0]:
+                    watts = (steps[-1][1] - steps[0][1]) / (steps[-1][0] - steps[0][0])
+                clocks = clocks[len(clocks) // 2:]
                 rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
                 rec["sclk_samples"] = len(clocks)
                 rec["board_watts_mean"] = round(watts, 1)

@@ -773,7 +773,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   auto step = [&](int ps, auto parity, auto group) __attribute__((always_inline)) {
     constexpr bool GA = decltype(group)::value == 0;
     if (GA && FP8) issue_step(ps);
+    // BF16: the wave in its matrix phase takes issue priority over the other
+    // wave of its SIMD, so a ready MFMA does not wait behind vector work (1.3%
+    // faster; FP8, whose vector phase is the longer half, ran 0.8% slower)
+    if constexpr (!FP8) __builtin_amdgcn_s_setprio(1);
     matrix_work(ps, parity);
+    if constexpr (!FP8) __builtin_amdgcn_s_setprio(0);
     barrier(!GA);
     if (GA && !FP8) issue_step(ps);
     vector_work(ps);
