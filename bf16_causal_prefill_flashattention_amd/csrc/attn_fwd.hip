@@ -763,8 +763,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   //   group A: matrix(p) | barrier | vector(p), wait | barrier
   //   group B: matrix(p), wait | barrier | vector(p), loads(p+1) | barrier
   // Group A issues its loads of step p before its matrix work for FP8 and at
-  // the start of its vector work for BF16: the FP8 softmax is the longer half
-  // of a phase and the BF16 matrix work is (the loads take the CU's load path
+  // the start of its vector work for BF16: the FP8 softmax is at least as long
+  // as its matrix work and the BF16 matrix work is the longer half (the loads take the CU's load path
   // for a few hundred cycles, so they go where the wave has slack).  Group B
   // issues at the end of its vector work.  Every load of step p is waited for
   // at the barrier that ends phase 2p+1, when all waves have issued theirs.
@@ -775,7 +775,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     if (GA && FP8) issue_step(ps);
     // BF16: the wave in its matrix phase takes issue priority over the other
     // wave of its SIMD, so a ready MFMA does not wait behind vector work (1.3%
-    // faster; FP8, whose vector phase is the longer half, ran 0.8% slower)
+    // faster).  FP8 ran 0.8% slower with it: its vector half is as long as its
+    // matrix half, and delaying it delays the barrier.
     if constexpr (!FP8) __builtin_amdgcn_s_setprio(1);
     matrix_work(ps, parity);
     if constexpr (!FP8) __builtin_amdgcn_s_setprio(0);
