@@ -41,8 +41,10 @@ def hipcc() -> str:
 
 
 # Per-source flags.  The attention kernel never sees NaN inputs (scores are
-# finite or -inf), so fmax needs no NaN quieting; the quantizer keeps strict IEEE.
-EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"]}
+# finite or -inf), so fmax needs no NaN quieting.  The quantizer keeps strict
+# IEEE and forms no FMA from a separate multiply and add, so its codes stay
+# bit-identical to a step-by-step fp32 evaluation.
+EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "quantize_fp8.hip": ["-ffp-contract=off"]}
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:
