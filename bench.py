@@ -20,14 +20,27 @@ the probabilities scaled per block as well under ``block64.p_block_scale``.
 ``roofline`` describes the attention kernel (the dominant one): its algorithmic
 FLOPs per launch divided by its average launch duration, measured with HIP
 events on the launch stream inside the timed region, against the dense MFMA
-peak of its dtype.  ``sclk_mhz`` is the graphics clock sampled (amdsmi) over
-the second half of 2.5 s of back-to-back launches after the timed region, and
-``frac_at_sclk`` the fraction of the peak scaled from its 2.4 GHz to that clock
-(the random operand data holds the clock below 2.4 GHz).  ``cpu_baseline`` times the CPU oracle (test
-infrastructure, untuned) on a bounded sample of the same workload.
+peak of its dtype.  Before the counted warmup launches, each leg runs at least
+``--prewarm`` seconds (default 1.5) of back-to-back launches so that the clock
+has settled when the timed region starts.  ``sclk_mhz`` is the graphics clock
+sampled (amdsmi, every 10 ms) during the timed region, ``sclk_prewarm_mhz`` the
+same over the second half of the pre-warm, and ``frac_at_sclk`` the fraction of
+the peak scaled from its 2.4 GHz to the timed region's clock (the random
+operand data holds the clock below 2.4 GHz).
+
+``cpu_baseline`` times the CPU oracle (test infrastructure, untuned) on a
+bounded sample of the same workload: whole heads, every row, one head per
+worker process of a pool as large as the host cores this process may use (at
+most 16); ``cores`` is that worker count.  The same oracle outputs are compared
+with the output of the timed launches, and ``parity`` reports the relative
+Frobenius error over the compared heads (and per head), the gate of the
+workload's dtype (BF16 1e-2, FP8 6e-2 against the oracle on the dequantized
+inputs), and whether the GPU quantizer's codes and scales of those heads equal
+the oracle quantizer's.  The BF16 leg gets its own ``parity`` the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-bf16] [--no-cpu-baseline] [--no-chunk] [--no-block64]
+                       [--prewarm SECONDS] [--no-bf16] [--no-cpu-baseline]
+                       [--no-chunk] [--no-block64]
        python bench.py --clock-study [--study-seconds S]
 
 ``--clock-study`` measures how the input data moves the sustained clock and
@@ -53,7 +66,7 @@ if ROOT not in sys.path:
 METRIC = "causal attn fwd TFLOP/s (FP8 & BF16, d=128, N=32K) + % of MFMA peak"
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense MFMA, published
 PAGES_FP8_HD128_32K = 2672.0  # TFLOP/s, FP8 causal fwd, hd128, N=32K, Gaussian, on MI355X (the pages' figure)
-ATTN_KERNEL_SOURCES = ["attn_fwd.hip", "device_common.hpp"]
+ATTN_KERNEL_SOURCES = ["attn_fwd_impl.hpp", "device_common.hpp"]  # the kernel template and its helpers
 
 
 def code_tokens(text: str) -> str:
@@ -103,59 +116,99 @@ def amdsmi_handle():
     return _AMDSMI[0]
 
 
-def sample_sclk(step, ms_per_launch: float, seconds: float = 2.5):
-    """Mean graphics clock in MHz (amdsmi's current-clock reading, sampled every
-    20 ms) over about `seconds` of back-to-back launches of `step`, run after
-    the timed region; None where amdsmi is unavailable.  Only the second half of
-    the samples counts: the reading is a moving average that lags the load by a
-    good part of a second."""
-    import threading
+class ClockSampler:
+    """Samples the graphics clock (amdsmi's current-clock reading, MHz) every
+    10 ms on a thread while it runs; no-op where amdsmi is unavailable."""
 
+    def __init__(self):
+        self.handle = amdsmi_handle()
+        self.samples = []  # (perf_counter seconds, MHz)
+        self._stop = None
+        self._th = None
+
+    def __enter__(self):
+        import threading
+
+        if self.handle is None:
+            return self
+        import amdsmi
+
+        self._stop = threading.Event()
+
+        def sample():
+            while not self._stop.wait(0.01):
+                try:
+                    mhz = amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX)["clk"]
+                    self.samples.append((time.perf_counter(), mhz))
+                except Exception:
+                    pass
+
+        self._th = threading.Thread(target=sample, daemon=True)
+        self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+
+    def mean(self, t0: float, t1: float):
+        c = [m for t, m in self.samples if t0 <= t <= t1]
+        return (round(sum(c) / len(c), 1), len(c)) if c else (None, 0)
+
+
+def timed_launches(step, steps: int, warmup: int, prewarm_s: float, stream):
+    """Pre-warm (back-to-back launches for at least prewarm_s seconds), then
+    `warmup` untimed launches, then `steps` timed ones bracketed by device
+    synchronisation, each with HIP events recorded on `stream`, the stream the
+    kernels are launched on.  The clock is sampled throughout.  Returns (wall
+    ms per step, per-launch event ms, clock dict)."""
     import torch
 
-    handle = amdsmi_handle()
-    if handle is None:
-        return None
-    import amdsmi
+    with ClockSampler() as clk:
+        torch.cuda.synchronize()
+        tp0 = time.perf_counter()
+        while time.perf_counter() - tp0 < prewarm_s:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+        tp1 = time.perf_counter()
+        for _ in range(warmup):
+            step()
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in events:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sclk, n = clk.mean(t0, t1)
+    sclk_pre, npre = clk.mean((tp0 + tp1) / 2, tp1)
+    clock = {"sclk_mhz": sclk, "sclk_samples": n, "sclk_prewarm_mhz": sclk_pre, "prewarm_s": round(tp1 - tp0, 2)}
+    return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events], clock
 
-    n = max(20, int(seconds * 1e3 / max(ms_per_launch, 1e-3)))
-    clocks, stop = [], threading.Event()
 
-    def sample():
-        while not stop.wait(0.02):
-            try:
-                clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-            except Exception:
-                pass
-
-    th = threading.Thread(target=sample, daemon=True)
-    th.start()
-    for _ in range(n):
-        step()
-    torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    clocks = clocks[len(clocks) // 2:]
-    return round(sum(clocks) / len(clocks), 1) if clocks else None
-
-
-def run_gpu(w, steps: int, warmup: int):
-    """Time `steps` attention launches (after `warmup` untimed ones) on inputs
-    resident in HBM.  Returns (wall ms per step, per-launch event ms, front-end
-    ms or None)."""
+def run_gpu(w, steps: int, warmup: int, prewarm_s: float):
+    """Time `steps` attention launches of workload w on inputs resident in HBM.
+    Returns a dict: wall ms per step, per-launch event ms, front-end ms (FP8),
+    clock readings, and on the host the output of the timed launches, the BF16
+    activations and (FP8) the codes and scales, for the parity check."""
     import torch
 
     import bf16_causal_prefill_flashattention_amd as miattn
     from bf16_causal_prefill_flashattention_amd.inputs import make_qkv
 
     dev = torch.device("cuda:0")
-    q, k, v = make_qkv(w)
-    q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))  # BF16 activations in HBM
+    hq, hk, hv = (t.to(torch.bfloat16) for t in make_qkv(w))  # BF16 activations
+    q, k, v = (t.to(dev) for t in (hq, hk, hv))
     fp8 = w.dtype == "fp8"
     block64 = fp8 and w.scales == "block64"
     out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)  # every kernel below is enqueued on this stream
     front_ms = None
+    codes = None
     if fp8:
         cq = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         ck = torch.empty(k.shape, dtype=torch.uint8, device=dev)
@@ -183,33 +236,88 @@ def run_gpu(w, steps: int, warmup: int):
                 fe.append(e0.elapsed_time(e1))
         front_ms = sorted(fe)[len(fe) // 2]
         args = (cq, ck, cv, sq, sk, sv)
+        if not block64:
+            codes = tuple(t.cpu() for t in args)
     else:
         args = (q, k, v)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         if block64:
             miattn.attn_fwd_block64(*args, out=out, with_lse=False, p_block_scale=w.p_block_scale)
         else:
             miattn.attn_fwd(*args, out=out)
-        if ev is not None:
-            ev[1].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+    ms, attn_ms, clock = timed_launches(step, steps, warmup, prewarm_s, stream)
+    return {"ms": ms, "attn_ms": attn_ms, "front_ms": front_ms, "clock": clock,
+            "out": out.cpu(), "inputs": (hq, hk, hv), "codes": codes}
+
+
+def parity_tasks(w, res, heads):
+    """Oracle tasks for whole heads of workload w (B = 1): the BF16 activations
+    the timed launches read (FP8: the activations the front end quantized, with
+    its codes and scales), and the output of the timed launches."""
+    import numpy as np
+
+    q, k, v = res["inputs"]
+    out, codes = res["out"], res["codes"]
+    grp = w.Hq // w.Hkv
+    f32 = lambda t: np.ascontiguousarray(t.float().numpy())  # noqa: E731
+    tasks = []
+    for h in heads:
+        g = h // grp
+        t = {"key": h, "q": f32(q[0, :, h]), "k": f32(k[0, :, g]), "v": f32(v[0, :, g]), "out": f32(out[0, :, h]),
+             "fp8": {"hadamard": w.hadamard} if w.dtype == "fp8" else None}
+        if codes is not None:
+            cq, ck, cv, sq, sk, sv = codes
+            t["codes"] = (cq[0, :, h].numpy(), ck[0, :, g].numpy(), cv[0, :, g].numpy(),
+                          float(sq[0, h]), float(sk[0, g]), float(sv[0, g]))
+        tasks.append(t)
+    return tasks
+
+
+def oracle_heads(pool, w, res):
+    """Run the oracle on one wave of whole heads (as many as the pool has
+    workers, spread over the heads) and compare them with the timed launches'
+    output.  Returns (parity dict, heads, wall seconds)."""
+    import numpy as np
+
+    from oracle.pool import summarize
+
+    n = min(w.Hq, pool.workers)
+    heads = sorted({int(h) for h in np.linspace(0, w.Hq - 1, n).round()})
+    tasks = parity_tasks(w, res, heads)
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    attn_ms = [a.elapsed_time(b) for a, b in events]
-    ms_per_step = (t1 - t0) * 1e3 / steps
-    sclk = sample_sclk(step, ms_per_step)
-    return ms_per_step, attn_ms, front_ms, sclk
+    results = pool.run(tasks)
+    el = time.perf_counter() - t0
+    s = summarize(results)
+    tol = 6e-2 if w.dtype == "fp8" else 1e-2
+    parity = {"rel_fro": float(f"{s['rel_fro']:.4e}"), "per_head_max": float(f"{s['per_head_max']:.4e}"),
+              "tolerance": tol, "pass": bool(s["rel_fro"] <= tol and s["per_head_max"] <= tol),
+              "heads": heads, "rows": "all", "codes_equal": s["codes_equal"],
+              "reference": "fp64 oracle on the dequantized inputs" if w.dtype == "fp8" else
+              "fp64 oracle on the BF16 inputs"}
+    return parity, heads, el
+
+
+def cpu_baseline(pool, w, res):
+    """The oracle (as it stands) on a bounded sample of the workload: one wave
+    of whole heads, every row, one head per worker process.  FP8: oracle
+    quantization of the head's Q, K, V plus exact attention on the dequantized
+    values; BF16: exact attention on the BF16 values.  Also returns the parity
+    of those heads against the timed launches' output."""
+    parity, heads, el = oracle_heads(pool, w, res)
+    flops = float(w.B) * len(heads) * float(w.N) ** 2 * (w.d_qk + w.d_v)
+    base = {
+        "value": round(flops / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(pool.workers),
+        "kind": "oracle",
+        "sample": f"{len(heads)} of {w.Hq} query heads (all {w.N} rows each) of {w.name}, "
+                  f"{'quantize + ' if w.dtype == 'fp8' else ''}fp64 attention, one head per worker process "
+                  f"({pool.workers} workers, one BLAS thread each), {el:.1f} s",
+        "seconds": round(el, 2),
+    }
+    return base, parity
 
 
 def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
@@ -219,10 +327,10 @@ def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
     return float(B) * Hq * (2.0 * Nq * Nk - float(Nq) ** 2) * (d_qk + d_v)
 
 
-def run_chunk(w, Nq: int, steps: int, warmup: int):
+def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float):
     """Time attn_fwd_chunk (with LSE) for the last Nq positions of workload w's
     FP8 sequence; inputs quantized by the library and resident in HBM.
-    Returns (wall ms per step, per-launch event ms)."""
+    Returns (wall ms per step, per-launch event ms, clock dict)."""
     import torch
 
     import bf16_causal_prefill_flashattention_amd as miattn
@@ -238,29 +346,16 @@ def run_chunk(w, Nq: int, steps: int, warmup: int):
     lse = torch.empty((w.B, w.Hq, Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         miattn.attn_fwd_chunk(cq, ck, cv, sq, sk, sv, out=out, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
+    return timed_launches(step, steps, warmup, prewarm_s, stream)
 
 
 PEAK_SCLK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
 
 
-def roofline(w, attn_ms, flops=None, sclk=None):
+def roofline(w, attn_ms, flops=None, clock=None):
     flops = w.causal_flops if flops is None else flops
     avg_s = sum(attn_ms) / len(attn_ms) * 1e-3
     achieved = flops / avg_s / 1e12
@@ -277,57 +372,11 @@ def roofline(w, attn_ms, flops=None, sclk=None):
         "avg_launch_ms": round(avg_s * 1e3, 4),
         "min_launch_ms": round(min(attn_ms), 4),
         "flops_per_launch": flops,
-        # sustained graphics clock over back-to-back launches, and the fraction
-        # of the peak scaled to that clock (the MFMA work per cycle is fixed)
-        "sclk_mhz": sclk,
-        "frac_at_sclk": None if not sclk else round(achieved / (peak * sclk / PEAK_SCLK_MHZ), 4),
-    }
-
-
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle (as it stands) on a bounded sample: whole heads, one at a
-    time, until the time budget is spent.  FP8: oracle quantization of the
-    head's Q, K, V plus exact attention on the dequantized values; BF16:
-    exact attention on the BF16 values."""
-    import numpy as np
-    import torch
-
-    from bf16_causal_prefill_flashattention_amd.inputs import make_qkv
-    from oracle import attn_ref, dequantize_ref, quantize_ref
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    q, k, v = make_qkv(w)
-    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))  # the same BF16 activations the GPU step reads
-    grp = w.Hq // w.Hkv
-    done = 0
-    t0 = time.perf_counter()
-    while done < w.Hq and (time.perf_counter() - t0) < budget_s:
-        h = done
-        g = h // grp
-        qh, kh, vh = q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1]
-        if w.dtype == "fp8":
-            cq, sq = quantize_ref(qh, w.hadamard)
-            ck, sk = quantize_ref(kh, w.hadamard)
-            cv, sv = quantize_ref(vh, False)
-            attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
-        else:
-            attn_ref(qh, kh, vh)
-        done += 1
-    el = time.perf_counter() - t0
-    flops = float(w.B) * done * float(w.N) ** 2 * (w.d_qk + w.d_v)
-    return {
-        "value": round(flops / el / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{done} of {w.Hq} query heads (all {w.N} rows each) of {w.name}, "
-                  f"{'quantize + ' if w.dtype == 'fp8' else ''}fp64 attention, {el:.1f} s",
-        "seconds": round(el, 2),
+        # graphics clock during the timed region (after the pre-warm), and the
+        # fraction of the peak scaled to that clock (the MFMA work per cycle is fixed)
+        **(clock or {}),
+        "frac_at_sclk": None if not (clock or {}).get("sclk_mhz") else
+        round(achieved / (peak * clock["sclk_mhz"] / PEAK_SCLK_MHZ), 4),
     }
 
 
@@ -438,6 +487,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--prewarm", type=float, default=1.5,
+                    help="seconds of back-to-back launches before the counted warmup of every leg")
     ap.add_argument("--workload", default="fp8_mha_n32k")
     ap.add_argument("--bf16-workload", default="bf16_mha_n32k")
     ap.add_argument("--no-bf16", action="store_true")
@@ -447,7 +498,6 @@ def main(argv=None):
     ap.add_argument("--clock-study", action="store_true")
     ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the warmup, run one plain elementwise copy (torch.neg) that reads and writes "
                          "this many bytes: the reference kernel of known traffic for scaling HBM counters")
@@ -456,17 +506,31 @@ def main(argv=None):
         print("bench.py measures one GPU only: the path is a single-GPU kernel and the library has no "
               "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
         return 2
-
-    import torch
+    if args.clock_study:
+        return clock_study(args.study_seconds)
 
     from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    pool = None
+    if not args.no_cpu_baseline:
+        # the oracle's worker processes start before this process touches the GPU
+        from oracle.pool import HeadPool
+
+        pool = HeadPool()
+    try:
+        return bench(args, w, WORKLOADS, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def bench(args, w, WORKLOADS, pool):
+    import torch
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    if args.clock_study:
-        return clock_study(args.study_seconds)
-    w = WORKLOADS[args.workload]
     amdsmi_handle()  # initialised before any launch
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
@@ -474,7 +538,8 @@ def main(argv=None):
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    ms, attn_ms, front_ms, sclk = run_gpu(w, args.steps, args.warmup)
+    res = run_gpu(w, args.steps, args.warmup, args.prewarm)
+    ms = res["ms"]
     value = w.causal_flops / (ms * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -495,53 +560,59 @@ def main(argv=None):
             "outlier_channels": w.outliers, "hadamard": w.hadamard,
             "step": "one causal attention launch",
         },
-        "roofline": roofline(w, attn_ms, sclk=sclk),
+        "roofline": roofline(w, res["attn_ms"], clock=res["clock"]),
     }
-    if front_ms is not None:
+    if res["front_ms"] is not None:
         rec["front_end"] = {"what": "quantize Q, K, V (bf16 -> e4m3, per-head amax/448), timed apart from the metric",
-                            "ms": round(front_ms, 4)}
+                            "ms": round(res["front_ms"], 4)}
+    if pool is not None:
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(pool, w, res)
+    del res
     if not args.no_bf16 and w.dtype == "fp8":
         wb = WORKLOADS[args.bf16_workload]
-        msb, attn_b, _, sclk_b = run_gpu(wb, args.steps, args.warmup)
+        rb = run_gpu(wb, args.steps, args.warmup, args.prewarm)
         rec["bf16"] = {
             "workload": wb.name,
-            "value": round(wb.causal_flops / (msb * 1e-3) / 1e12, 1),
-            "ms_per_step": round(msb, 4),
-            "roofline": roofline(wb, attn_b, sclk=sclk_b),
+            "value": round(wb.causal_flops / (rb["ms"] * 1e-3) / 1e12, 1),
+            "ms_per_step": round(rb["ms"], 4),
+            "roofline": roofline(wb, rb["attn_ms"], clock=rb["clock"]),
         }
+        if pool is not None:
+            rec["bf16"]["parity"] = oracle_heads(pool, wb, rb)[0]
+        del rb
     if not args.no_block64 and w.name == "fp8_mha_n32k":
         wq = WORKLOADS["fp8_mha_n32k_block64"]
-        msq, attn_q, front_q, sclk_q = run_gpu(wq, args.steps, args.warmup)
+        rq = run_gpu(wq, args.steps, args.warmup, args.prewarm)
         rec["block64"] = {
             "workload": f"{wq.name}: the same inputs with one power-of-two scale per 64 positions "
                         "(K and V scales applied by the scaled MFMAs)",
-            "value": round(wq.causal_flops / (msq * 1e-3) / 1e12, 1),
-            "ms_per_step": round(msq, 4),
-            "front_end_ms": round(front_q, 4),
-            "roofline": roofline(wq, attn_q, sclk=sclk_q),
+            "value": round(wq.causal_flops / (rq["ms"] * 1e-3) / 1e12, 1),
+            "ms_per_step": round(rq["ms"], 4),
+            "front_end_ms": round(rq["front_ms"], 4),
+            "roofline": roofline(wq, rq["attn_ms"], clock=rq["clock"]),
         }
+        del rq
         wp = WORKLOADS["fp8_mha_n32k_block64_pscale"]
-        msp, attn_p, _, sclk_p = run_gpu(wp, args.steps, args.warmup)
+        rp = run_gpu(wp, args.steps, args.warmup, args.prewarm)
         rec["block64"]["p_block_scale"] = {
             "workload": f"{wp.name}: probabilities also scaled per block by powers of two",
-            "value": round(wp.causal_flops / (msp * 1e-3) / 1e12, 1),
-            "ms_per_step": round(msp, 4),
-            "roofline": roofline(wp, attn_p, sclk=sclk_p),
+            "value": round(wp.causal_flops / (rp["ms"] * 1e-3) / 1e12, 1),
+            "ms_per_step": round(rp["ms"], 4),
+            "roofline": roofline(wp, rp["attn_ms"], clock=rp["clock"]),
         }
+        del rp
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
-        msc, attn_c = run_chunk(w, Nq, args.steps, args.warmup)
+        msc, attn_c, clock_c = run_chunk(w, Nq, args.steps, args.warmup, args.prewarm)
         fl = chunk_flops(w.B, w.Hq, Nq, w.N, w.d_qk, w.d_v)
         rec["chunk"] = {
             "workload": f"{w.name} chunk: last {Nq} positions against {w.N} keys, LSE written",
             "Nq": Nq, "Nk": w.N,
             "value": round(fl / (msc * 1e-3) / 1e12, 1),
             "ms_per_step": round(msc, 4),
-            "roofline": roofline(w, attn_c, fl),
+            "roofline": roofline(w, attn_c, fl, clock=clock_c),
         }
         rec["chunk"]["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     rec["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(rec), flush=True)
     return 0

@@ -16,6 +16,9 @@ Entry points (same names as the C ABI):
   with_lse=True, softmax_scale=None, p_block_scale=False)`` (FP8 with
   per-64-position scales, optionally power-of-two scaled probabilities)
 * ``attn_quantize_fp8_block64(x, hadamard=False, out=None, scale=None)``
+* ``attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None,
+  with_lse=True, softmax_scale=None, scales="head", p_mode="lean")`` (FP8
+  with a chosen scale granularity and probability mode, ``P_MODES``)
 * ``attn_status_string(status)``, ``attn_version()``
 
 and ``flash_attn_func``, a ``flash_attn_func``-style drop-in over them (BSHD
@@ -32,6 +35,7 @@ __all__ = [
     "attn_fwd",
     "attn_fwd_block64",
     "attn_fwd_chunk",
+    "attn_fwd_fp8",
     "attn_quantize_fp8",
     "attn_quantize_fp8_block64",
     "attn_status_string",
@@ -42,12 +46,16 @@ __all__ = [
     "MiattnError",
     "DTYPE_BF16",
     "DTYPE_FP8_E4M3",
+    "P_MODES",
 ]
 
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3 = 1
 SRC_FP32 = 0
 SRC_BF16 = 1
+SCALES = {"head": 0, "block64": 1}
+# probability modes of the FP8 kernels (include/miattn.h, MIATTN_P_*)
+P_MODES = {"lean": 0, "lean_block": 1, "exact": 2, "exact_block": 3, "lean_tile": 4, "exact_tile": 5}
 
 _LIB = None
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +93,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_block64.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, ci,
                                      vp]
     lib.attn_fwd_block64.restype = ci
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, ci, ci,
+                                 vp]
+    lib.attn_fwd_fp8.restype = ci
     lib.attn_quantize_fp8_block64.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8_block64.restype = ci
     lib.attn_status_string.argtypes = [ci]
@@ -259,6 +270,39 @@ def attn_fwd_block64(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, wit
     )
     if st != 0:
         raise MiattnError("attn_fwd_block64", st)
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, with_lse=True, softmax_scale=None,
+                 scales="head", p_mode="lean"):
+    """FP8 causal attention with a chosen scale granularity (``scales``:
+    "head" -- q_scale [B,Hq], k_scale and v_scale [B,Hkv], as ``attn_fwd``; or
+    "block64" -- per-64-position scales, as ``attn_fwd_block64``) and
+    probability mode (``p_mode``: "lean", "lean_block", "lean_tile",
+    "exact", "exact_block", "exact_tile"; see ``P_MODES`` and MIATTN_P_* in
+    include/miattn.h).
+    q [B,Nq,Hq,d_qk], k [B,Nk,Hkv,d_qk], v [B,Nk,Hkv,d_v] e4m3 codes; query row
+    i sees keys j <= i + Nk - Nq.  Returns ``(out, lse)`` as
+    ``attn_fwd_chunk``."""
+    torch = _torch()
+    if scales not in SCALES:
+        raise ValueError(f"scales must be one of {sorted(SCALES)}")
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {sorted(P_MODES)}")
+    if q.dtype == torch.bfloat16:
+        raise TypeError("attn_fwd_fp8 takes e4m3 codes")
+    block64 = scales == "block64"
+    q, k, v, _, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale, block64)
+    out = _out_tensor(out, q, B, Nq, Hq, dv)
+    lse = _lse_tensor(lse, with_lse, q, B, Hq, Nq)
+    st = load_library().attn_fwd_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, dqk, dv, ptr_s[0], ptr_s[1], ptr_s[2],
+        0.0 if softmax_scale is None else float(softmax_scale), SCALES[scales], P_MODES[p_mode],
+        _stream_handle(q.device),
+    )
+    if st != 0:
+        raise MiattnError("attn_fwd_fp8", st)
     return out, lse
 
 

@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["attn_fwd.hip", "quantize_fp8.hip", "miattn_api.cpp"]
+ATTN_FP8 = [f"attn_fwd_fp8_{s}_d{d}.hip" for s in ("head", "block64") for d in (128, 192)]
+SOURCES = ATTN_FP8 + ["attn_fwd_bf16.hip", "attn_fwd.hip", "quantize_fp8.hip", "miattn_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -44,7 +45,8 @@ def hipcc() -> str:
 # finite or -inf), so fmax needs no NaN quieting.  The quantizer keeps strict
 # IEEE and forms no FMA from a separate multiply and add, so its codes stay
 # bit-identical to a step-by-step fp32 evaluation.
-EXTRA_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"], "quantize_fp8.hip": ["-ffp-contract=off"]}
+EXTRA_FLAGS = {src: ["-fno-honor-nans"] for src in ATTN_FP8 + ["attn_fwd_bf16.hip"]}
+EXTRA_FLAGS["quantize_fp8.hip"] = ["-ffp-contract=off"]
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:

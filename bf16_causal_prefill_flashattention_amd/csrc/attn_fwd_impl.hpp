@@ -1,0 +1,956 @@
+// Kernel template of the causal forward attention (included by the
+// translation units that instantiate its variants).
+#pragma once
+
+// Causal forward (prefill) attention for gfx950: O = softmax(Q K^T tau + mask) V.
+//
+// Page legend: [P1] "Zyphra ZYFA: 1.76x FP8 FlashAttention Speedup on AMD
+// MI355X"; [P3] "Zyphra 开源 ZYFA：面向 AMD MI355X 的 FP8 FlashAttention，最高提速
+// 1.76 倍".
+//
+// What is computed: exact causal softmax attention, evaluated tile by tile with
+// an online softmax so the N x N score matrix never reaches HBM ([P1] "Why
+// prefill attention deserves dedicated optimization").  FP8 e4m3 inputs carry
+// per-(batch, head) fp32 scales folded in before the softmax; both matrix
+// products accumulate in FP32 ([P1] "ZYFA's performance and accuracy data";
+// [P3] "为什么 FP8 注意力在 MI355X 上表现不佳？").  Output is BF16.
+//
+// Queries may be the last Nq positions of a longer key sequence (Nq <= Nk: one
+// chunk of a chunked prefill against the keys and values before it); query row
+// i then sits at position i + Nk - Nq.  Optionally the natural-log sum of exp
+// of each query's scaled scores (LSE) is written, which is what combining the
+// results of separate key ranges needs.
+//
+// Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
+// (batch, query head); each wave owns 32 queries.  Key tiles hold 128 keys
+// (FP8), 96 (BF16, d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips the tiles
+// wholly above its queries and masks only the tiles that cross its diagonal.
+//
+// Matrix layout.  A wave computes S^T = K_tile * Q^T (keys on MFMA rows,
+// queries on MFMA columns), so lane l owns query (l % 32) and holds half of the
+// tile's scores for it; the other half sits in lane l ^ 32.  The output is
+// accumulated transposed, O^T += V^T * P^T: the probabilities leave the S^T
+// accumulator straight into the MFMA B operand, in an order of keys that the
+// V^T operand reproduces when it is read from LDS.
+//
+// Two-group ping-pong.  A tile's softmax depends on that tile's S = K Q^T
+// MFMAs, and its P.V product on the softmax, so within one wave the two kinds
+// of work of a tile follow each other.  (Independent vector instructions do
+// issue while the wave's own MFMAs execute: on gfx950, 128 independent FMAs
+// interleaved with 16 FP8 32x32x64 MFMAs took the MFMAs' 980 cycles.)  Here the
+// 8 waves form two groups (waves 0-3 and 4-7, one wave of each per SIMD) that
+// run the same loop one phase apart, separated by workgroup barriers, so one
+// wave's softmax runs beside the other's matrix work:
+//   phase 2p   : group A matrix work  | group B vector work
+//   phase 2p+1 : group A vector work  | group B matrix work
+// where "matrix work" of step p is P_{p-1} V_{p-1} followed by S_p = K_p Q^T,
+// and "vector work" of step p is the online softmax of S_p.  This is the
+// two-wave overlap the pages describe ([P3] "ZYFA 如何工作？"), ordered here by
+// barriers instead of per-instruction scheduling.
+//
+// Data movement.  K and V tiles go from HBM/L2 straight into LDS with buffer
+// loads that write LDS (no register staging).  K and V rows are stored with an
+// XOR swizzle of their 16-byte chunks so that the rows one operand read
+// touches fall in distinct LDS banks; the V^T operand is read with the
+// transposing LDS reads of gfx950.  Two LDS buffers each for K and V; the loads
+// of step p (issued in phase 2p, or early in phase 2p+1) are waited for at the
+// end of phase 2p+1.  Rows at or beyond Nq
+// (queries) or Nk (keys), and whole tiles past the last one a workgroup needs,
+// load as zeros (buffer bounds), so ragged tiles and the loads of the final
+// steps need no branches; keys >= Nk lie above the diagonal of every valid
+// query and are masked.
+//
+// FP8 scale granularity.  Either one fp32 scale per (batch, head) for each of
+// Q, K, V, folded into the score multiplier and the output, or one scale per
+// 64 positions: Q's per-wave block scale (a wave's 32 queries lie in one block)
+// goes into the score multiplier, and the power-of-two K and V block scales are
+// applied by the scaled MFMAs as E8M0 exponents (a 32-key QK block and a 64-key
+// P.V k-step each lie in one 64-key block), at no vector cost.  The exponents of
+// a work item's key tiles are staged in LDS, one word per 128-key tile.
+//
+// FP8 probabilities.  Lean P writes the e4m3 code of 2^x straight from one FMA
+// on the log2-domain score x; the exact mode uses exp2 and the hardware
+// conversion ([P3] "ZYFA 如何工作？" weighs the two).  Both multiply the
+// probabilities by a fixed 2^6 first.  Lean codes reach about 13 octaves below
+// that (the exact conversion's subnormals about 2.5 further), so key blocks
+// whose scores lie far below the running max would round to zero; a shift
+// keeps them: each query's probabilities of a 128-key tile (tile mode, the
+// default) or of a 64-key P.V step (block mode, the pages' per-64-key
+// power-of-two scaling of P undone by the scaled MFMA) are shifted up by k
+// octaves, k = floor(running max - their max), and the P.V MFMA scales them
+// back by the E8M0 exponent 2^-k.  The scaled MFMAs read the exponent of a
+// 32-key block of column j from lane j + 32 b, while each lane holds half of
+// both blocks of its k-step, so both lanes of a query use one exponent (the
+// pair's max).  The row sum of a shifted step: block mode sums it in a
+// 32x32x64 MFMA against an all-ones A with the same exponents; tile mode sums
+// the step's codes on their own and scales the sum back on the vector side.
+//
+// Probabilities.  The running max is only raised when a tile's max exceeds it
+// by more than a small threshold, so most tiles skip the rescale of the output
+// accumulator.  The row sum is taken from the rounded probabilities that feed
+// the P.V product ([P3] "ZYFA 如何工作？", rounded row sums), with one extra
+// small MFMA per P.V k-step against a 0/1 selector matrix (16x16x128 for FP8,
+// 16x16x32 for BF16).  It runs on the matrix core with the other MFMAs of the
+// wave: the vector-side dot-product instructions share the matrix pipeline and
+// stall behind the other wave's MFMAs.  FP8 probabilities are scaled by a fixed
+// power of two before rounding to e4m3, which the row sum cancels.
+#include "device_common.hpp"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
+namespace miattn {
+
+namespace {
+
+constexpr int kThreads = 512;  // 8 waves, two per SIMD
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
+
+template <bool FP8, int DQK, int DV>
+struct Cfg {
+  static constexpr int EB = FP8 ? 1 : 2;     // bytes per element
+  // keys per tile.  A phase carries a roughly fixed cost (barriers, the first
+  // operand reads), so larger tiles amortise it; BF16 at d = 128 stops at 96
+  // keys (128 would not fit two waves' registers per SIMD), and BF16 at d = 192
+  // stays at 64 (its 384-byte K rows would not split into whole 1 KB load
+  // blocks per wave at 96)
+  static constexpr int BN = FP8 ? 128 : (DQK == 128 ? 96 : 64);
+  static constexpr int NBLK = BN / 32;       // 32-key MFMA blocks per tile
+  static constexpr int KROW = DQK * EB;      // bytes of one K row
+  static constexpr int VROW = DV * EB;       // bytes of one V row
+  static constexpr int KCH = KROW / 16;      // 16-byte chunks per K row
+  static constexpr int VCH = VROW / 16;      // 16-byte chunks per V row
+  // K rows are stored unpadded with their 16-byte chunks XOR-swizzled inside
+  // groups of KG chunks (k_swizzle), V rows likewise (v_swizzle)
+  static constexpr int KG = KCH % 16 == 0 ? 16 : (KCH % 8 == 0 ? 8 : 4);
+  static constexpr int K_TILE = BN * KROW;
+  static constexpr int V_TILE = BN * VROW;
+  static constexpr int K_BLOCKS = BN * KCH / 64;  // 1 KB LDS-load blocks per K tile
+  static constexpr int V_BLOCKS = BN * VCH / 64;
+  static constexpr int K_PER_WAVE = K_BLOCKS / kWaves;
+  static constexpr int V_PER_WAVE = V_BLOCKS / kWaves;
+  static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
+  static constexpr int LDS_BYTES = 2 * V_TILE + 2 * K_TILE;
+  // log2-domain growth of the running max tolerated before rescaling, and the
+  // power-of-two shift applied to FP8 probabilities: p <= 2^(THRESH + SHIFT),
+  // whose lean-P code round(8 (THRESH + SHIFT) + C0) = 126 is e4m3's largest
+  // finite value (448) for THRESH + SHIFT < 8.855
+  static constexpr float THRESH = FP8 ? 2.75f : 8.0f;
+  static constexpr float SHIFT = FP8 ? 6.0f : 0.0f;
+  static_assert(K_BLOCKS % kWaves == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks per wave");
+  static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
+};
+
+// XOR applied to the 16-byte chunk index of V row `key` in LDS.  It spreads the
+// rows that one transposing read touches over distinct banks: FP8 reads 8 keys
+// {0-3, 8-11} + base per lane group (key bits 1 and 3 vary), BF16 reads 4
+// consecutive keys (bits 0 and 1 vary).
+template <bool FP8>
+__device__ __forceinline__ int v_swizzle(int key) {
+  if constexpr (FP8)
+    return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2);
+  else
+    return (key & 3) << 2;
+}
+
+// XOR applied inside a group of KG 16-byte chunks of K row `row` in LDS.  The
+// 16 lanes that one quarter of a 16-byte operand read serves (rows r..r+15, one
+// chunk) then fall in 16 distinct groups of four banks: 128-byte rows (FP8,
+// d=128) alternate two 8-chunk bank halves, so the swizzle takes rows in
+// pairs; 256-byte rows (BF16) start in the same bank, so every row gets its
+// own; 192-byte rows (FP8 MLA) cycle four 4-chunk groups; 384-byte rows (BF16
+// MLA) alternate halves like 128-byte ones.
+template <class C>
+__device__ __forceinline__ int k_swizzle(int row) {
+  if constexpr (C::KROW == 256)
+    return row & 15;
+  else if constexpr (C::KROW == 192)
+    return (row >> 2) & 3;
+  else
+    return (row >> 1) & 7;
+}
+// LDS position (chunk index within the row) of logical chunk `ch` of K row `row`
+// (an involution: it also maps a position back to its logical chunk)
+template <class C>
+__device__ __forceinline__ int k_chunk_pos(int row, int ch) {
+  return (ch & ~(C::KG - 1)) | ((ch ^ k_swizzle<C>(row)) & (C::KG - 1));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, I1).
+template <int I0, int I1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
+
+// Buffer load of 16 bytes per lane written straight to LDS: lane i's bytes land
+// at lds_block + 16 i (lds_block is wave-uniform).  Offsets at or beyond the
+// buffer size load zeros.
+//
+// Issued as inline assembly: the compiler then does not track these loads, so
+// it does not make the LDS reads of the current tile wait for the loads of the
+// next one (it cannot prove they touch different buffers).  The explicit
+// "s_waitcnt vmcnt(0)" before the barrier that ends the next phase is what
+// orders them.  The LDS address goes in M0 through an operand constraint, so
+// the compiler itself writes M0 and knows what it holds.
+//
+// Hazards the compiler does not resolve for inline assembly: an LDS-writing
+// buffer load must not follow an SALU write of M0 directly (one wait state,
+// the s_nop 0 here), and must not read an SGPR written by a VALU instruction
+// (v_readfirstlane) within five wait states -- rsrc_words ends with those.
+__device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, const uint8_t* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_block);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
+// Buffer resource words for raw 16-byte loads over [base, base + bytes): 32-bit
+// offsets, out-of-range offsets read zeros.  Wave-uniform.  The words come out
+// of v_readfirstlane (VALU writes of SGPRs); the empty-bodied s_nop 4 that
+// takes them as operands puts five wait states between those writes and any
+// buffer load that reads them.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r = {(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+             (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+  asm volatile("s_nop 4" : "+s"(r));
+  return r;
+}
+
+// Bytes of rows [kb, min(kb + BN, end)) of a tile at pitch `pitch`, on the
+// scalar unit (left to itself the compiler clamps with a vector med3 and a
+// vector multiply, then moves the result back to a scalar register: a chain of
+// dependent instructions in front of every tile load).
+__device__ __forceinline__ uint32_t tile_bytes(int end, int kb, int bn, uint32_t pitch) {
+  int r;
+  asm("s_sub_i32 %0, %1, %2\n\t"
+      "s_min_i32 %0, %0, %3\n\t"
+      "s_max_i32 %0, %0, 0\n\t"
+      "s_mul_i32 %0, %0, %4"
+      : "=&s"(r)
+      : "s"(end), "s"(kb), "s"(bn), "s"(pitch)
+      : "scc");
+  return (uint32_t)r;
+}
+
+// Workgroup barrier that also orders every memory access around it in the
+// compiler; with wait_loads the wave first waits for its own outstanding
+// global/buffer loads (including the LDS-writing ones).
+__device__ __forceinline__ void barrier(bool wait_loads) {
+  if (wait_loads)
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float lane_xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS reads (gfx950).  Within each group of 16 lanes, tr8: lane i
+// byte j = byte (i % 8) of the 8 bytes addressed by lane 2j + i/8; tr16: lane i
+// element j = element (i % 4) of the 4 halves addressed by lane 4j + i/4.
+__device__ __forceinline__ i32x2v lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)p);
+}
+__device__ __forceinline__ i16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+template <bool FP8>
+struct QOp;
+template <>
+struct QOp<true> {
+  using T = i32x8;
+};
+template <>
+struct QOp<false> {
+  using T = bf16x8;
+};
+
+template <int DV>
+struct RowState {
+  f32x16 o[DV / 32];  // O^T accumulator: lane owns query l % 32, channels 32d + 8i + 4hl + j
+  float m;            // running max, log2 domain
+  f32x4 l4;           // the full row sum (every entry)
+  f32x16 l16;         // the same, from the all-ones row-sum MFMA (shift per 64-key step)
+  f32x4 rs;           // shift per tile: row sum of the last P.V step's codes (every entry)
+  float lrun;         // shift per tile: the row sum, scaled back step by step
+  float sprev;        // shift per tile: 2^-k of the probabilities in pk
+  float kc;           // lean P: integer code offset K = 8 (SHIFT - m) + C0 (m kept on that grid)
+};
+
+// Probability shifts of the FP8 kernels: none (a fixed 2^SHIFT), one power of
+// two per query and 64-key P.V step, or one per query and key tile.
+enum PShift { kShiftNone = 0, kShiftStep = 1, kShiftTile = 2 };
+
+// Lean P.  The e4m3 code of 2^x (x in [-6, 8]) is 8x + 56 at integer x and
+// linear in between, so a probability's code is round(8 x + C0) with x = s c -
+// m + SHIFT.  One FMA computes MAGIC + 8 s c + K (K = 8 (SHIFT - m) + C0, an
+// integer because m is kept on that grid): with MAGIC = 1.5 * 2^23 the float's
+// low mantissa byte is the rounded code.  One max against MAGIC clamps codes below 0
+// (the float then equals MAGIC: code 0, also for masked -inf scores) and writes
+// that low byte into the packed probability word (SDWA byte select).  C0 centres
+// the error of the linear mantissa: 55.66 minimises the largest log error over
+// an octave.
+constexpr float kLeanC0 = 55.66f;
+constexpr float kLeanMagic = 12582912.0f;  // 1.5 * 2^23
+
+// Codes of four scores into one word, first score in the low byte.
+__device__ __forceinline__ uint32_t lean_p4(float s0, float s1, float s2, float s3, float c8, float b8, float magic) {
+  const float t0 = __builtin_fmaf(s0, c8, b8), t1 = __builtin_fmaf(s1, c8, b8);
+  const float t2 = __builtin_fmaf(s2, c8, b8), t3 = __builtin_fmaf(s3, c8, b8);
+  uint32_t w;
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+      : "=v"(w) : "v"(t0), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t1), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t2), "v"(magic));
+  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+      : "+v"(w) : "v"(t3), "v"(magic));
+  return w;
+}
+
+template <class C, bool FP8, int DQK, int DV>
+struct Wave {
+  static constexpr int NBLK = C::NBLK;
+  // per-lane LDS byte offsets (relative to a buffer)
+  int k_lane[C::KG];        // K operand: row l % 32, chunk group position (k-half folded in)
+  int v_lane[DV / 32];      // V^T operand per 32-channel block
+  uint32_t k_dma[C::K_PER_WAVE];
+  uint32_t v_dma[C::V_PER_WAVE];
+  typename QOp<FP8>::T q[C::QK_STEPS];
+  f32x16 s[NBLK];
+  uint32_t pk[FP8 ? C::BN / 8 : C::BN / 4];  // this lane's probabilities of the tile (half its keys), MFMA B-operand order
+  uint32_t pscale;  // probability shift: E8M0 exponent of this query's P (k-step ks in byte ks, or byte 0 per tile)
+  RowState<DV> st;
+};
+
+}  // namespace
+
+// One work item: the kBM queries of query tile qt of (batch, head) bh, against
+// all keys up to the last of them.  Key tiles are visited in increasing order,
+// or from the last one down when `rev` is set (the softmax is the same in any
+// key order; the order only decides which tiles the workgroups of an XCD read
+// at the same time).  Called by every thread of the workgroup; leaves no load
+// in flight and no wave reading LDS when it returns.
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN>
+__device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
+                                          bool rev) {
+  static_assert(!BS || FP8, "block scales are an FP8 feature");
+  static_assert(PSH == kShiftNone || FP8, "probability shifts are an FP8 feature");
+  constexpr bool PS = PSH == kShiftStep, PT = PSH == kShiftTile;
+  static_assert(!LEAN || FP8, "lean-P codes are e4m3 codes");
+  using C = Cfg<FP8, DQK, DV>;
+  constexpr int NBLK = C::NBLK;
+  constexpr int BN = C::BN;
+  uint8_t* const Vs = smem;                 // V buffers 0, 1
+  uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int grp = w >> 2;  // 0: matrix work on even phases, 1: on odd phases
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int off = Nk - Nq;  // position of query row 0 in the key sequence
+  const int b = bh / p.Hq, h = bh % p.Hq, g = h / (p.Hq / p.Hkv);
+  const int q0 = qt * kBM;
+  // SIMD s runs waves s (group 0) and s + 4 (group 1); they own query blocks
+  // 2s and 2s + 1, so both groups have work on the diagonal tiles.
+  const int qblk = 2 * (w & 3) + grp;
+  const int qw0 = q0 + 32 * qblk;  // first query of this wave
+  const int my_q = qw0 + l32;      // query row owned by this lane (position my_q + off)
+
+  const uint32_t q_pitch = (uint32_t)p.Hq * C::KROW;  // bytes between consecutive positions
+  const uint32_t k_pitch = (uint32_t)p.Hkv * C::KROW;
+  const uint32_t v_pitch = (uint32_t)p.Hkv * C::VROW;
+  const uint8_t* Q = static_cast<const uint8_t*>(p.q) + ((size_t)b * Nq * p.Hq + h) * C::KROW;
+  const uint8_t* K = static_cast<const uint8_t*>(p.k) + ((size_t)b * Nk * p.Hkv + g) * C::KROW;
+  const uint8_t* V = static_cast<const uint8_t*>(p.v) + ((size_t)b * Nk * p.Hkv + g) * C::VROW;
+
+  float c = p.sm_scale_log2;  // log2-domain score scale (dequantisation folded in for FP8)
+  float sv = 1.f;
+  if constexpr (FP8 && BS) {
+    const int nbq = (Nq + 63) / 64;
+    c *= p.q_scale[((size_t)b * p.Hq + h) * nbq + min(qw0, Nq - 1) / 64];
+  } else if constexpr (FP8) {
+    c *= p.q_scale[b * p.Hq + h] * p.k_scale[b * p.Hkv + g];
+    sv = p.v_scale[b * p.Hkv + g];
+  }
+
+  Wave<C, FP8, DQK, DV> wv;
+
+  // ---- per-lane LDS offsets of the operand reads
+  // chunk ct of a K-operand read is logical chunk ct + (2 or 1) * hl of the
+  // lane's row l % 32 (the rows of block blk are l % 32 + 32 blk, same swizzle)
+#pragma unroll
+  for (int ct = 0; ct < C::KG; ++ct)
+    wv.k_lane[ct] = l32 * C::KROW + 16 * ((ct ^ (hl * (FP8 ? 2 : 1)) ^ k_swizzle<C>(l32)) & (C::KG - 1));
+  {
+    const int grp16 = lane >> 4, s16 = lane & 15;
+    const int lhl = grp16 >> 1, gc = grp16 & 1;
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db) {
+      if constexpr (FP8) {
+        // source lane s16 = 2j + hh reads 8 bytes: key 8(j/4) + 4hl + j%4,
+        // channels 32db + 16gc + 8hh .. +8
+        const int j = s16 >> 1, hh = s16 & 1;
+        const int key = 8 * (j >> 2) + 4 * lhl + (j & 3);
+        const int ch = 2 * db + gc;
+        wv.v_lane[db] = key * C::VROW + 16 * (ch ^ v_swizzle<true>(key)) + 8 * hh;
+      } else {
+        // source lane s16 = 4j + qq reads 4 halves: key 4hl + j, channels
+        // 32db + 16gc + 4qq .. +4
+        const int j = s16 >> 2, qq = s16 & 3;
+        const int key = 4 * lhl + j;
+        const int ch = 4 * db + 2 * gc + (qq >> 1);
+        wv.v_lane[db] = key * C::VROW + 16 * (ch ^ v_swizzle<false>(key)) + 8 * (qq & 1);
+      }
+    }
+  }
+  // ---- per-lane global offsets of the tile loads (tile-relative, the same for every tile)
+#pragma unroll
+  for (int i = 0; i < C::K_PER_WAVE; ++i) {
+    const int blk = w + kWaves * i;
+    const int pos = 64 * blk + lane, row = pos / C::KCH, slot = pos % C::KCH;
+    wv.k_dma[i] = (uint32_t)row * k_pitch + 16u * k_chunk_pos<C>(row, slot);
+  }
+#pragma unroll
+  for (int i = 0; i < C::V_PER_WAVE; ++i) {
+    const int blk = w + kWaves * i;
+    const int pos = 64 * blk + lane, key = pos / C::VCH, slot = pos % C::VCH;
+    wv.v_dma[i] = (uint32_t)key * v_pitch + 16u * (slot ^ v_swizzle<FP8>(key));
+  }
+
+  const int kend = min(q0 + kBM, Nq) + off;  // keys visible to the workgroup's last query, plus one
+  const int T = (kend + BN - 1) / BN;        // key tiles of the workgroup
+  // tiles this wave needs: keys up to the position of its last valid query
+  const int Tw = qw0 < Nq ? ((min(qw0 + 31, Nq - 1) + off) / BN + 1) : 0;
+  // steps [s_lo, s_hi) carry the wave's tiles; step s visits tile tile_of(s),
+  // and steps at or beyond T map to tile T (an empty load range)
+  const int s_lo = rev ? T - Tw : 0, s_hi = rev ? T : Tw;
+  const int t_base = rev ? T - 1 : 0, t_dir = rev ? -1 : 1;
+  // (unsigned min: the -1 of a downward walk past tile 0 also maps to T)
+  auto tile_of = [&](int s) __attribute__((always_inline)) {
+    return (int)min((uint32_t)(t_base + t_dir * s), (uint32_t)T);
+  };
+
+  // tiles at or beyond T load with an empty range (zeros, no memory access), so
+  // the loads need no branches
+  // (read-first-lane: keeps the load-range arithmetic on the scalar unit)
+  const int krows_end = __builtin_amdgcn_readfirstlane(min(Nk, T * BN));
+  auto issue_k = [&](int t, int buf) __attribute__((always_inline)) {
+    const int kb = t * BN;
+    const i32x4 rk = rsrc_words(K + (size_t)min(kb, krows_end) * k_pitch, tile_bytes(krows_end, kb, BN, k_pitch));
+#pragma unroll
+    for (int i = 0; i < C::K_PER_WAVE; ++i) {
+      const int blk = w + kWaves * i;
+      load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
+    }
+  };
+  auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+    const int kb = t * BN;
+    const i32x4 rv = rsrc_words(V + (size_t)min(kb, krows_end) * v_pitch, tile_bytes(krows_end, kb, BN, v_pitch));
+#pragma unroll
+    for (int i = 0; i < C::V_PER_WAVE; ++i) {
+      const int blk = w + kWaves * i;
+      load_to_lds(rv, wv.v_dma[i], Vs + buf * C::V_TILE + 1024 * blk);
+    }
+  };
+  // loads of step p: K tile p+1 and V tile p
+  auto issue_step = [&](int pstep) __attribute__((always_inline)) {
+    issue_k(tile_of(pstep + 1), (pstep + 1) & 1);
+    issue_v(tile_of(pstep), pstep & 1);
+  };
+
+  // ---- Q^T operand in registers.  BF16: k-step kk = channels [16kk, 16kk+16),
+  // lane half hl holds 8 of them; FP8: k-step kk = channels [64kk, 64kk+64), 32 each.
+  {
+    const uint32_t rows = (uint32_t)max(0, min(32, Nq - qw0));
+    const auto rq = make_rsrc(Q + (size_t)min(qw0, Nq) * q_pitch, rows * q_pitch);
+#pragma unroll
+    for (int kk = 0; kk < C::QK_STEPS; ++kk) {
+      if constexpr (FP8) {
+        const uint32_t off = (uint32_t)l32 * q_pitch + kk * 64 + hl * 32;
+        const i32x4 lo = bload16(rq, off), hi = bload16(rq, off + 16);
+        wv.q[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        wv.q[kk] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)l32 * q_pitch + kk * 32 + hl * 16));
+      }
+    }
+    // Pass the Q registers through an empty asm so the compiler waits for these
+    // loads here, once, instead of at their first use inside the loop (where
+    // the wait would also stall on the tile loads in flight).
+#pragma unroll
+    for (int kk = 0; kk < C::QK_STEPS; ++kk) asm volatile("" : "+v"(wv.q[kk]));
+  }
+
+#pragma unroll
+  for (int d = 0; d < DV / 32; ++d) wv.st.o[d] = zero16();
+  wv.st.m = -1e30f;
+  wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (PS) wv.st.l16 = zero16();
+  if constexpr (PT) {
+    wv.st.rs = f32x4{0.f, 0.f, 0.f, 0.f};
+    wv.st.lrun = 0.f;
+    wv.st.sprev = 1.f;
+  }
+  wv.st.kc = 0.f;
+  // Row-sum selector (A operand of the 16x16 row-sum MFMA): 1.0 where the lane
+  // group's parity matches its row group's parity, else 0.  Lane l then finds
+  // the sum over the k-step's keys for its own query l % 32 in every entry of
+  // its D registers.
+  const bool sel_on = ((lane >> 4) & 1) == (((lane & 15) >> 2) & 1);
+  const int sel_w = sel_on ? (FP8 ? 0x38383838 : 0x3f803f80) : 0;  // e4m3 / bf16 ones
+  const i32x8 sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
+  // With probability block scaling the row sum is a 32x32x64 MFMA against an
+  // all-ones A: its B exponents are read per (column, 32-key block) as in the
+  // P.V product (the 16x16x128 form reads one column's exponents from the lanes
+  // of a single query, but that column also holds another query's keys).
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+
+  // E8M0 exponents of the K tile (bytes 0, 1: its two 64-key blocks) and V tile
+  // (bytes 2, 3) of the current matrix phase (block scales only)
+  // (unit exponents 127 without block scales: only the probability scale applies)
+  uint32_t kexp = 0, vexp = BS ? 0u : 0x7f7f7f7fu;
+
+  // ---- matrix work of step pstep: P_{pstep-1} V_{pstep-1}, then S_pstep = K_pstep Q^T.
+  // The products form one list of MFMAs (PV first, then QK with the k-steps
+  // outermost so consecutive MFMAs are independent); the LDS operand of MFMA
+  // i+1 is read while MFMA i runs.
+  constexpr int PV_OPS = FP8 ? (BN / 64) * (DV / 32) : (BN / 16) * (DV / 32);
+  constexpr int QK_OPS = NBLK * C::QK_STEPS;
+  using AOp = typename std::conditional<FP8, i32x8, i32x4>::type;
+  auto fetch = [&](int i, const uint8_t* vb, const uint8_t* kb) __attribute__((always_inline)) -> AOp {
+    AOp a;
+    if (i < PV_OPS) {
+      if constexpr (FP8) {
+        const int ks = i / (DV / 32), db = i % (DV / 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const i32x2v t = lds_tr8(vb + wv.v_lane[db] + (64 * ks + 32 * (r >> 1) + 16 * (r & 1)) * C::VROW);
+          a[2 * r] = t[0];
+          a[2 * r + 1] = t[1];
+        }
+      } else {
+        const int chunk = i / (DV / 32), db = i % (DV / 32);
+        const i16x4 t0 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk) * C::VROW);
+        const i16x4 t1 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk + 8) * C::VROW);
+        const i32x2v u0 = __builtin_bit_cast(i32x2v, t0), u1 = __builtin_bit_cast(i32x2v, t1);
+        a = i32x4{u0[0], u0[1], u1[0], u1[1]};
+      }
+    } else {
+      const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
+      const uint8_t* row = kb + blk * 32 * C::KROW;
+      if constexpr (FP8) {
+        // logical chunks 4kk + 2hl + {0, 1}
+        const int c0 = 4 * kk, c1 = 4 * kk + 1;
+        const i32x4 lo = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
+        const i32x4 hi = lds_load16(row + wv.k_lane[c1 & (C::KG - 1)] + 16 * (c1 & ~(C::KG - 1)));
+        a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int c0 = 2 * kk;  // logical chunk 2kk + hl
+        a = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
+      }
+    }
+    return a;
+  };
+  auto mma = [&](int i, const AOp& a) __attribute__((always_inline)) {
+    if (i < PV_OPS) {
+      if constexpr (FP8) {
+        const int ks = i / (DV / 32), db = i % (DV / 32);
+        const i32x8 pb = {(int)wv.pk[8 * ks + 0], (int)wv.pk[8 * ks + 1], (int)wv.pk[8 * ks + 2],
+                          (int)wv.pk[8 * ks + 3], (int)wv.pk[8 * ks + 4], (int)wv.pk[8 * ks + 5],
+                          (int)wv.pk[8 * ks + 6], (int)wv.pk[8 * ks + 7]};
+        if constexpr (PS) {
+          if (db == 0)
+            wv.st.l16 = ks == 0 ? mfma_fp8_32x32x64_sab<0, 0>(ones, pb, wv.st.l16, 127, (int)wv.pscale)
+                                : mfma_fp8_32x32x64_sab<0, 1>(ones, pb, wv.st.l16, 127, (int)wv.pscale);
+          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
+                                : mfma_fp8_32x32x64_sab<3, 1>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
+        } else if constexpr (PT) {
+          // the step's row sum on its own (scaled back on the vector side)
+          if (db == 0)
+            wv.st.rs = mfma_fp8_16x16x128(sel, pb, ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : wv.st.rs);
+          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
+                                : mfma_fp8_32x32x64_sab<3, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
+        } else {
+          if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
+          if constexpr (BS)
+            wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
+                                  : mfma_fp8_32x32x64_sa<3>(a, pb, wv.st.o[db], (int)vexp);
+          else
+            wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
+        }
+      } else {
+        const int chunk = i / (DV / 32), db = i % (DV / 32);
+        const i32x4 pw = {(int)wv.pk[4 * chunk], (int)wv.pk[4 * chunk + 1], (int)wv.pk[4 * chunk + 2],
+                          (int)wv.pk[4 * chunk + 3]};
+        if (db == 0)
+          wv.st.l4 = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(sel, sel, 0, 1, 2, 3)),
+                                        __builtin_bit_cast(bf16x8, pw), wv.st.l4);
+        wv.st.o[db] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pw), wv.st.o[db]);
+      }
+    } else {
+      const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
+      const f32x16 acc = kk == 0 ? zero16() : wv.s[blk];
+      if constexpr (FP8 && BS)
+        wv.s[blk] = blk < 2 ? mfma_fp8_32x32x64_sa<0>(a, wv.q[kk], acc, (int)kexp)
+                            : mfma_fp8_32x32x64_sa<1>(a, wv.q[kk], acc, (int)kexp);
+      else if constexpr (FP8)
+        wv.s[blk] = mfma_fp8_32x32x64(a, wv.q[kk], acc);
+      else
+        wv.s[blk] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), wv.q[kk], acc);
+    }
+  };
+  // LDS reads of the operand of list entry i, and MFMAs it issues
+  auto n_reads = [](int i) constexpr { return i < PV_OPS ? (FP8 ? 4 : 2) : (FP8 ? 2 : 1); };
+  auto n_mfma = [](int i) constexpr { return (i < PV_OPS && i % (DV / 32) == 0) ? 2 : 1; };
+  // MFMAs [i0, i1) of the list; the operand of MFMA i+2 is read before MFMA i
+  // issues (three operand buffers), an order pinned with scheduling groups.
+  auto run_ops = [&](auto i0_tag, auto i1_tag, const uint8_t* vb, const uint8_t* kb) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
+    AOp buf[3];
+    buf[0] = fetch(I0, vb, kb);
+    __builtin_amdgcn_sched_group_barrier(0x100, n_reads(I0), 0);
+    if constexpr (I0 + 1 < I1) {
+      buf[1] = fetch(I0 + 1, vb, kb);
+      __builtin_amdgcn_sched_group_barrier(0x100, n_reads(I0 + 1), 0);
+    }
+    static_for<I0, I1>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 2 < I1) {
+        buf[(i + 2 - I0) % 3] = fetch(i + 2, vb, kb);
+        __builtin_amdgcn_sched_group_barrier(0x100, n_reads(i + 2), 0);
+      }
+      mma(i, buf[(i - I0) % 3]);
+      __builtin_amdgcn_sched_group_barrier(0x008, n_mfma(i), 0);
+    });
+  };
+  auto matrix_work = [&](int pstep, auto parity) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(parity)::value;  // pstep & 1
+    const uint8_t* vb = Vs + (1 - PAR) * C::V_TILE;       // V tile pstep-1
+    const uint8_t* kb = Ks + PAR * C::K_TILE;  // K tile pstep
+    // One instruction sequence for every step the wave takes part in (a single
+    // variant keeps the register allocation tight): at step s_lo the P.V
+    // product multiplies the zero probabilities the item starts with (by a
+    // zero-filled or fully loaded V buffer), and at step s_hi the scores of a
+    // tile the wave does not need are computed and never read.
+    if (pstep >= s_lo && pstep <= s_hi) {
+      if constexpr (BS) {
+        kexp = ebuf[tile_of(pstep)];
+        vexp = ebuf[tile_of(pstep - 1)];
+      }
+      run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
+    }
+  };
+
+  // ---- vector work of step pstep: online softmax of S_pstep -> probabilities.
+  auto vector_work = [&](int pstep) __attribute__((always_inline)) {
+    if (pstep < s_lo || pstep >= s_hi) return;
+    const int kb = tile_of(pstep) * BN;
+    if (kb + BN - 1 > qw0 + off) {  // the tile crosses this wave's diagonal: mask keys above each query
+      // key offset k of register r is visible iff k <= lim; the sign of lim - k
+      // selects -inf bit by bit (no per-element compare masks held in SGPRs)
+      const int lim = my_q + off - kb - 4 * hl;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t hide = (uint32_t)((lim - (blk * 32 + 8 * (r >> 2) + (r & 3))) >> 31);
+          const float x = wv.s[blk][r];  // scalar copy before the bit cast
+          wv.s[blk][r] = __uint_as_float((hide & 0xff800000u) | (~hide & __float_as_uint(x)));
+        }
+    }
+    // row max: four independent chains of 3-input max (two new values each);
+    // with probability block scaling, chains 2ks and 2ks+1 cover exactly this
+    // lane's keys of k-step ks (blocks 2ks, 2ks+1)
+    float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float& m = mc[PS ? 2 * (blk >> 1) + ((r >> 1) & 1) : (blk * 8 + r / 2) & 3];
+        m = fmaxf(fmaxf(m, wv.s[blk][r]), wv.s[blk][r + 1]);
+      }
+    float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+    mx = lane_xor32_max(mx);
+    const float mt = mx * c;
+    // shift per tile: the row sum of the previous step's probabilities (which
+    // were 2^k too large) joins the running sum before any rescale
+    if constexpr (PT) wv.st.lrun = __builtin_fmaf(wv.st.rs[0], wv.st.sprev, wv.st.lrun);
+    if (__any(mt > wv.st.m + C::THRESH)) {  // wave-uniform; rare once the max settles
+      float m_new = fmaxf(wv.st.m, mt);
+      if constexpr (LEAN) {
+        // round the new max up onto the grid where K = 8 (SHIFT - m) + C0 is an integer
+        const float kc = floorf(8.f * (C::SHIFT - m_new) + kLeanC0);
+        const bool up = mt > wv.st.m;
+        m_new = up ? C::SHIFT + (kLeanC0 - kc) * 0.125f : wv.st.m;
+        wv.st.kc = up ? kc : wv.st.kc;
+      }
+      const float alpha = fast_exp2(wv.st.m - m_new);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) wv.st.o[d] *= alpha;
+      if constexpr (PS)
+        wv.st.l16 *= alpha;
+      else if constexpr (PT)
+        wv.st.lrun *= alpha;
+      else
+        wv.st.l4 *= alpha;
+      wv.st.m = m_new;
+    }
+    const float bias = C::SHIFT - wv.st.m;
+    if constexpr (FP8) {
+      // pk[8ks + 4hb + i] holds keys 64ks + 32hb + 8i + 4hl + {0..3}
+      // Probability block scaling: k = floor(running max - the query's max
+      // over the 64 keys of k-step ks) octaves, in [0, 126]; the probabilities
+      // of the k-step are 2^k times larger (lean P: codes up by 8k) and the
+      // MFMA scale is 2^-k (a k-step whose keys are all masked gets k = 126
+      // and codes 0).  Without it, k = 0.
+      // Shift per tile: one k = min(floor(running max - the query's max over
+      // the tile), 126) for the whole tile (k may be slightly negative while
+      // the tile max runs ahead of the lazy running max; the largest
+      // probability is then at most 2^SHIFT).
+      float kst[NBLK / 2];
+      if constexpr (PT) {
+        const float kt = fminf(floorf(wv.st.m - mt), 126.f);
+        const uint32_t e = (uint32_t)(127 - (int)kt);  // E8M0 exponent of 2^-k
+        wv.pscale = e;
+        wv.st.sprev = __uint_as_float(e << 23);  // 2^-k
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) kst[ks] = kt;
+      }
+      if constexpr (PS) {
+        uint32_t ps = 0;
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) {
+          const float bmax = lane_xor32_max(fmaxf(mc[2 * ks], mc[2 * ks + 1]));
+          kst[ks] = fminf(fmaxf(floorf(__builtin_fmaf(-bmax, c, wv.st.m)), 0.f), 126.f);
+          ps |= (uint32_t)(127 - (int)kst[ks]) << (8 * ks);
+        }
+        wv.pscale = ps;
+      }
+      if constexpr (LEAN) {
+        // lean P: one FMA gives MAGIC + the code (low mantissa byte), one SDWA
+        // max clamps it and inserts the byte
+        const float c8 = 8.f * c, b8 = kLeanMagic + wv.st.kc, magic = kLeanMagic;
+        float bks[NBLK / 2];  // code offset of k-step ks
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) bks[ks] = PSH != kShiftNone ? __builtin_fmaf(8.f, kst[ks], b8) : b8;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            wv.pk[4 * blk + i] = lean_p4(wv.s[blk][4 * i], wv.s[blk][4 * i + 1], wv.s[blk][4 * i + 2],
+                                         wv.s[blk][4 * i + 3], c8, bks[blk >> 1], magic);
+      } else {
+        // exact P: exp2 and the hardware round-to-nearest-even e4m3 conversion
+        float bexp[NBLK / 2];  // log2-domain offset of k-step ks
+#pragma unroll
+        for (int ks = 0; ks < NBLK / 2; ++ks) bexp[ks] = PSH != kShiftNone ? bias + kst[ks] : bias;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              e[jj] = fast_exp2(__builtin_fmaf(wv.s[blk][4 * i + jj], c, bexp[blk >> 1]));
+            wv.pk[4 * blk + i] = pack_fp8x4(e[0], e[1], e[2], e[3]);
+          }
+      }
+    } else {
+      // pk[2r' + e] with r' = 8blk + ... : register pair (r, r+1) of block blk
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(wv.s[blk][2 * i], c, bias));
+          const float p1 = fast_exp2(__builtin_fmaf(wv.s[blk][2 * i + 1], c, bias));
+          const uint32_t pp = pack_bf16x2(p0, p1);
+          wv.pk[8 * blk + i] = pp;
+        }
+    }
+  };
+
+  // ---- prologue: the tiles' scale exponents (block scales) into LDS; K tile 0
+  // into buffer 0; V buffer 1 (read by the empty P.V product of step 0) and the
+  // probabilities start at zero.
+  if constexpr (BS) {
+    // word t: E8M0 of K blocks 2t, 2t+1 and V blocks 2t, 2t+1 (indices past the
+    // last block repeat it: those keys load as zeros and are masked)
+    const int nbk = (Nk + 63) / 64;
+    const float* ksc = p.k_scale + ((size_t)b * p.Hkv + g) * nbk;
+    const float* vsc = p.v_scale + ((size_t)b * p.Hkv + g) * nbk;
+    for (int t = tid; t <= T; t += kThreads) {
+      const int i0 = min(2 * t, nbk - 1), i1 = min(2 * t + 1, nbk - 1);
+      const uint32_t k0 = __float_as_uint(ksc[i0]), k1 = __float_as_uint(ksc[i1]);
+      const uint32_t v0 = __float_as_uint(vsc[i0]), v1 = __float_as_uint(vsc[i1]);
+      ebuf[t] = ((k0 >> 23) & 0xffu) | (((k1 >> 23) & 0xffu) << 8) | (((v0 >> 23) & 0xffu) << 16) |
+                (((v1 >> 23) & 0xffu) << 24);
+    }
+  }
+  issue_k(tile_of(0), 0);
+#pragma unroll
+  for (int i = 0; i < C::V_TILE / (16 * kThreads); ++i)
+    lds_store16(Vs + C::V_TILE + 16 * (tid + kThreads * i), i32x4{0, 0, 0, 0});
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(wv.pk) / sizeof(wv.pk[0])); ++i) wv.pk[i] = 0u;
+  wv.pscale = 0x7f7f7f7fu;  // unit scales
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (grp == 1) {
+    issue_step(0);
+    barrier(false);  // group B starts one phase later
+  }
+
+  // ---- main loop: steps 0..T (step T only drains P_{T-1} V_{T-1})
+  // Both groups run the same matrix/vector code; only where each issues its
+  // share of the tile loads and which barrier waits for them differ:
+  //   group A: matrix(p) | barrier | vector(p), wait | barrier
+  //   group B: matrix(p), wait | barrier | vector(p), loads(p+1) | barrier
+  // Group A issues its loads of step p before its matrix work for FP8 and at
+  // the start of its vector work for BF16: the FP8 softmax is at least as long
+  // as its matrix work and the BF16 matrix work is the longer half (the loads take the CU's load path
+  // for a few hundred cycles, so they go where the wave has slack).  Group B
+  // issues at the end of its vector work.  Every load of step p is waited for
+  // at the barrier that ends phase 2p+1, when all waves have issued theirs.
+  // No step runs past T, so no loads are issued for one either: an item ends
+  // with no load in flight that could land in the next item's first tiles.
+  auto step = [&](int ps, auto parity, auto group) __attribute__((always_inline)) {
+    constexpr bool GA = decltype(group)::value == 0;
+    if (GA && FP8) issue_step(ps);
+    // BF16: the wave in its matrix phase takes issue priority over the other
+    // wave of its SIMD, so a ready MFMA does not wait behind vector work (1.3%
+    // faster).  FP8 ran 0.8% slower with it: its vector half is as long as its
+    // matrix half, and delaying it delays the barrier.
+    if constexpr (!FP8) __builtin_amdgcn_s_setprio(1);
+    matrix_work(ps, parity);
+    if constexpr (!FP8) __builtin_amdgcn_s_setprio(0);
+    barrier(!GA);
+    if (GA && !FP8) issue_step(ps);
+    vector_work(ps);
+    if (!GA && ps + 1 <= T) issue_step(ps + 1);
+    barrier(GA);
+  };
+  // one loop per group, so the group decisions inside a step are compile-time
+  auto run_steps = [&](auto group) __attribute__((always_inline)) {
+    for (int ps = 0; ps <= T; ps += 2) {
+      step(ps, std::integral_constant<int, 0>{}, group);
+      if (ps + 1 <= T) step(ps + 1, std::integral_constant<int, 1>{}, group);
+    }
+  };
+  if (grp == 0)
+    run_steps(std::integral_constant<int, 0>{});
+  else
+    run_steps(std::integral_constant<int, 1>{});
+  if (grp == 0) barrier(false);
+
+  // ---- epilogue: normalise by the row sum and store BF16
+  if constexpr (PT) wv.st.lrun = __builtin_fmaf(wv.st.rs[0], wv.st.sprev, wv.st.lrun);  // the last step's P
+  const float lsum = PS ? wv.st.l16[0] : (PT ? wv.st.lrun : wv.st.l4[0]);
+  const float inv = sv / lsum;
+  if (my_q < Nq) {
+    // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
+    // log2 sum_j 2^x_j = m - SHIFT + log2(l); lanes l and l + 32 share a query
+    if (p.lse != nullptr && hl == 0)
+      p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(lsum)) * 0.69314718055994531f;
+    __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * Nq + my_q) * p.Hq + h) * DV;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = d * 32 + 8 * i + 4 * hl;
+        const i32x2 v2 = {(int)pack_bf16x2(wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv),
+                          (int)pack_bf16x2(wv.st.o[d][4 * i + 2] * inv, wv.st.o[d][4 * i + 3] * inv)};
+        *reinterpret_cast<i32x2*>(O + ch) = v2;
+      }
+    }
+  }
+}
+
+// Persistent workgroups (at most one per CU) walk a static list of work units.
+// A unit is a pair of query tiles of one (batch, head), the j-th from the end
+// and the j-th from the start of the causal triangle, so every unit costs about
+// the same and the workgroups finish together (separate per-tile workgroups
+// left CUs idle between workgroups and at the tail).  When there are no more
+// tiles than CUs, each workgroup takes a single tile instead (pairing would
+// only serialize short work).  Workgroup w runs on XCD w % 8 (round-robin
+// dispatch); when the (batch, head) count splits evenly over the 8 XCDs, XCD x
+// takes the heads bh = x (mod 8) and its workgroups sweep one head at a time,
+// so the K/V tiles they stream are shared in that XCD's L2.  The heavier tile of
+// a unit walks its keys upward and the lighter one downward: with units of
+// equal cost started together, every workgroup of an XCD then reads key tile t
+// at about the same moment in both halves (time t in the heavy half, a constant
+// minus t in the light half), so the workgroups stream two shared fronts of K/V
+// tiles instead of one stream each.
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
+  using C = Cfg<FP8, DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
+  const int nqt = (p.Nq + kBM - 1) / kBM;
+  const int nbh = p.B * p.Hq;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const bool single = (long long)nbh * nqt <= G;  // one tile per unit
+  const int per_bh = single ? nqt : (nqt + 1) / 2;  // units per (batch, head)
+  const bool by_xcd = (nbh % 8 == 0) && (G % 8 == 0);
+  const int rank = by_xcd ? wg / 8 : wg, nrank = by_xcd ? G / 8 : G;
+  const int nunit = by_xcd ? (nbh / 8) * per_bh : nbh * per_bh;
+  // one call site (the item body is large): the two tiles of a unit are
+  // iterations half = 0 (the later, heavier tile) and half = 1
+  int u = rank, half = 0;
+  while (u < nunit) {
+    const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
+    const int j = u % per_bh;
+    const int qt = half == 0 ? nqt - 1 - j : j;
+    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8, BS, PSH, LEAN>(p, smem, ebuf, bh, qt, !single && half == 1);
+    if (single) {
+      u += nrank;
+    } else {
+      u += half * nrank;
+      half ^= 1;
+    }
+  }
+}
+
+// Launch one variant (d_v = 128) on `grid` persistent workgroups.
+template <int DQK, bool FP8, bool BS, int PSH, bool LEAN>
+hipError_t launch_attn_variant(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// The probability modes of the FP8 kernels with one scale granularity.
+template <int DQK, bool BS>
+hipError_t launch_attn_fp8_modes(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  switch (p.p_mode) {
+    case kPLean: return launch_attn_variant<DQK, true, BS, kShiftNone, true>(p, grid, stream);
+    case kPLeanBlock: return launch_attn_variant<DQK, true, BS, kShiftStep, true>(p, grid, stream);
+    case kPLeanTile: return launch_attn_variant<DQK, true, BS, kShiftTile, true>(p, grid, stream);
+    case kPExact: return launch_attn_variant<DQK, true, BS, kShiftNone, false>(p, grid, stream);
+    case kPExactBlock: return launch_attn_variant<DQK, true, BS, kShiftStep, false>(p, grid, stream);
+    case kPExactTile: return launch_attn_variant<DQK, true, BS, kShiftTile, false>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace miattn

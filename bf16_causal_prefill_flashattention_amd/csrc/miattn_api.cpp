@@ -10,6 +10,11 @@
 
 #include "kernels.h"
 
+static_assert(MIATTN_P_LEAN == miattn::kPLean && MIATTN_P_LEAN_BLOCK == miattn::kPLeanBlock &&
+                  MIATTN_P_EXACT == miattn::kPExact && MIATTN_P_EXACT_BLOCK == miattn::kPExactBlock &&
+                  MIATTN_P_LEAN_TILE == miattn::kPLeanTile && MIATTN_P_EXACT_TILE == miattn::kPExactTile,
+              "the ABI's probability modes are the kernels' modes");
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -44,7 +49,7 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, co
 int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                  int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
                  const float* v_scale, double tau, void* stream, bool block64 = false,
-                 bool p_block_scale = false) {
+                 int p_mode = MIATTN_P_DEFAULT) {
   miattn::AttnParams p;
   p.q = q;
   p.k = k;
@@ -61,7 +66,7 @@ int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.Nk = Nk;
   p.sm_scale_log2 = (float)(1.4426950408889634 * tau);  // log2-domain softmax scale
   p.block64 = block64 ? 1 : 0;
-  p.p_block_scale = p_block_scale ? 1 : 0;
+  p.p_mode = dtype == MIATTN_DTYPE_FP8_E4M3 ? p_mode : miattn::kPLean;  // BF16 has one mode
   const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
@@ -146,7 +151,23 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
   if (B == 0 || Nq == 0) return MIATTN_OK;
   const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
   return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale, k_scale,
-                      v_scale, tau, stream, true, p_block_scale != 0);
+                      v_scale, tau, stream, true, p_block_scale != 0 ? MIATTN_P_LEAN_BLOCK : MIATTN_P_LEAN);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale, const float* v_scale,
+                 float softmax_scale, int scales, int p_mode, void* stream) {
+  if (scales != MIATTN_SCALES_HEAD && scales != MIATTN_SCALES_BLOCK64) return MIATTN_ERR_DTYPE;
+  if (p_mode < MIATTN_P_LEAN || p_mode > MIATTN_P_EXACT_TILE) return MIATTN_ERR_DTYPE;
+  if (!(softmax_scale == 0.0f || (std::isfinite(softmax_scale) && softmax_scale > 0.0f))) return MIATTN_ERR_VALUE;
+  const int st = validate_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale,
+                                   k_scale, v_scale);
+  if (st != MIATTN_OK) return st;
+  if (scales == MIATTN_SCALES_BLOCK64 && Nk > miattn::kBlock64MaxKeys) return MIATTN_ERR_SIZE;
+  if (B == 0 || Nq == 0) return MIATTN_OK;
+  const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
+  return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale, k_scale,
+                      v_scale, tau, stream, scales == MIATTN_SCALES_BLOCK64, p_mode);
 }
 
 int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,

@@ -21,7 +21,7 @@
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 4
+#define MIATTN_ABI_VERSION 5
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -63,7 +63,10 @@ extern "C" {
  * is code * scale with one fp32 scale per (batch, head):
  *   q_scale [B, Hq], k_scale [B, Hkv], v_scale [B, Hkv]   (device memory)
  * The scales are folded into the scores before the softmax and into the
- * output; probabilities are rounded to e4m3 for the P.V product.
+ * output; probabilities are rounded to e4m3 for the P.V product with lean P
+ * against each 128-key tile's own maximum (MIATTN_P_DEFAULT, see
+ * attn_fwd_fp8), so keys are lost only about 12 octaves below the maximum of
+ * their own tile.
  * dtype = MIATTN_DTYPE_BF16: the scale pointers are ignored and may be NULL.
  *
  * Sizes: B >= 0, N >= 0 (B == 0 or N == 0 is an empty call: success, nothing
@@ -205,6 +208,56 @@ int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* sc
 int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                      int Nq, int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale,
                      const float* v_scale, float softmax_scale, int p_block_scale, void* stream);
+
+/* Scale granularities of attn_fwd_fp8. */
+#define MIATTN_SCALES_HEAD 0    /* one fp32 scale per (batch, head), as attn_fwd */
+#define MIATTN_SCALES_BLOCK64 1 /* one scale per (batch, head, 64 positions), as attn_fwd_block64 */
+
+/* Probability modes of attn_fwd_fp8: how the softmax probabilities are rounded
+ * to e4m3 for the P.V product.  Every mode multiplies them by a fixed 2^6
+ * first (so the largest lies in [2^6, 2^8.75]) and divides the output by the
+ * sum of the rounded values. */
+#define MIATTN_P_LEAN 0        /* lean P: the e4m3 code of 2^x written from one FMA on the
+                                  log2-domain score x (attn_fwd's mode) */
+#define MIATTN_P_LEAN_BLOCK 1  /* lean P, and each query's probabilities of every 64-key step
+                                  shifted up by 2^k (k = octaves their max lies below the running
+                                  max, in [0, 126]); the scaled MFMAs multiply them by 2^-k */
+#define MIATTN_P_EXACT 2       /* exp2 and the hardware round-to-nearest-even e4m3 conversion */
+#define MIATTN_P_EXACT_BLOCK 3 /* exact, with the per-64-key shift of MIATTN_P_LEAN_BLOCK */
+#define MIATTN_P_LEAN_TILE 4   /* lean P, and each query's probabilities of every 128-key tile
+                                  shifted up by 2^k (k = min(floor(running max - their max), 126));
+                                  the scaled MFMAs multiply them by 2^-k */
+#define MIATTN_P_EXACT_TILE 5  /* exact, with the per-tile shift of MIATTN_P_LEAN_TILE */
+#define MIATTN_P_DEFAULT MIATTN_P_LEAN_TILE /* the mode of attn_fwd and attn_fwd_chunk on FP8 inputs */
+
+/* FP8 causal attention with a chosen scale granularity and probability mode.
+ *
+ * Defines: the causal forward attention of attn_fwd / attn_fwd_chunk (see
+ * there) on FP8 e4m3 inputs, with the probabilities formed in one of the ways
+ * the pages weigh against each other ([P3] "ZYFA 如何工作？": lean P, an
+ * e4m3 code written straight from the score, against exp plus conversion; and
+ * per-64-key power-of-two scaling of P undone by the scaled MFMA).
+ *
+ * Layout, sizes, softmax_scale, lse, stream, asynchrony and determinism as
+ * attn_fwd_chunk (scales = MIATTN_SCALES_HEAD: q_scale [B, Hq], k_scale and
+ * v_scale [B, Hkv]) or attn_fwd_block64 (scales = MIATTN_SCALES_BLOCK64:
+ * per-64-position scales, Nk <= 2^20).  attn_fwd_fp8(..., MIATTN_SCALES_HEAD,
+ * MIATTN_P_LEAN, ...) is attn_fwd_chunk on FP8 inputs, bit for bit;
+ * (MIATTN_SCALES_BLOCK64, MIATTN_P_LEAN or MIATTN_P_LEAN_BLOCK) is
+ * attn_fwd_block64 with p_block_scale 0 or 1.
+ * Input domain: in the modes without a shift (MIATTN_P_LEAN, MIATTN_P_EXACT),
+ * a probability more than about 12 octaves below its row's running max
+ * (2^-12 of it) is rounded to zero (below about 15 octaves) or to a subnormal
+ * e4m3 value; rows whose softmax mass lies largely that far below their
+ * largest score (long rows of keys whose magnitudes vary by block) lose that
+ * mass.  The block and tile modes round every 64-key step or 128-key tile
+ * against its own maximum, so only keys about 12 octaves below the maximum of
+ * their own step or tile are lost.
+ * scales or p_mode outside the values above: MIATTN_ERR_DTYPE.
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale, const float* v_scale,
+                 float softmax_scale, int scales, int p_mode, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

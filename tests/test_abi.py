@@ -32,10 +32,16 @@ def lib():
     return pkg.load_library()
 
 
-def test_header_declares_the_seven_entry_points():
+def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_quantize_fp8", "attn_quantize_fp8_block64",
-         "attn_status_string", "attn_version"])
+        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_fwd_fp8", "attn_quantize_fp8",
+         "attn_quantize_fp8_block64", "attn_status_string", "attn_version"])
+
+
+def test_probability_mode_constants_match_the_binding():
+    for name, code in pkg.P_MODES.items():
+        assert header_constant(f"MIATTN_P_{name.upper()}") == code
+    assert header_constant("MIATTN_SCALES_HEAD") == 0 and header_constant("MIATTN_SCALES_BLOCK64") == 1
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -138,6 +144,26 @@ def test_attn_fwd_block64_validation(lib, kw, expect):
     assert block64(lib, **kw) == expect
 
 
+def fp8(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=128, dv=128, qs=P, ks=P, vs=P,
+        tau=0.0, scales=0, pmode=0):
+    return lib.attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, qs, ks, vs, tau, scales, pmode, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), E_NULL), (dict(o=None), E_NULL), (dict(qs=None), E_NULL), (dict(vs=None), E_NULL),
+    (dict(Nq=21), E_SIZE), (dict(Hq=3, Hkv=2), E_SIZE),
+    (dict(Nq=8, Nk=(1 << 20) + 1, scales=1), E_SIZE),
+    (dict(dqk=64), E_SHAPE),
+    (dict(lse=P + 2), E_ALIGN), (dict(ks=P + 2), E_ALIGN),
+    (dict(tau=-1.0), E_VALUE),
+    (dict(scales=2), E_DTYPE), (dict(scales=-1), E_DTYPE), (dict(pmode=6), E_DTYPE), (dict(pmode=-1), E_DTYPE),
+    (dict(Nq=0), OK), (dict(B=0), OK), (dict(Nq=0, pmode=3, scales=1), OK),
+    (dict(Nq=0, q=None, k=None, v=None, o=None), OK),
+])
+def test_attn_fwd_fp8_validation(lib, kw, expect):
+    assert fp8(lib, **kw) == expect
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 
@@ -156,6 +182,12 @@ def test_binding_refuses_cpu_tensors():
         pkg.attn_fwd_block64(c, c, c, s, s, s)
     with pytest.raises(TypeError):
         pkg.attn_fwd_block64(q, q, q, s, s, s)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_fp8(c, c, c, s, s, s, p_mode="fast")
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_fp8(c, c, c, s, s, s, scales="tensor")
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_fp8(c, c, c, s, s, s)
 
 
 def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
