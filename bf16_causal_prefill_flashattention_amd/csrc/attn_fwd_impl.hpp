@@ -111,15 +111,23 @@ constexpr int kThreads = 512;  // 8 waves, two per SIMD
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 
-template <bool FP8, int DQK, int DV>
+// Keys per tile.  A phase carries a roughly fixed cost (barriers, the first
+// operand reads), so larger tiles amortise it.  FP8 at d = 128 with one scale
+// per head streams 192-key tiles; 128 where the per-64-key probability shift
+// (its four max chains) or the per-64-position scale exponents (one word per
+// 128-key tile) assume it, and at d = 192 (192-byte K rows do not split 192
+// keys into whole 1 KB load blocks per wave).  BF16 at d = 128 stops at 96
+// keys (128 would not fit two waves' registers per SIMD); BF16 at d = 192 stays
+// at 64 (its 384-byte K rows would not split into whole blocks at 96).
+template <bool FP8, int DQK, bool BS, int PSH>
+constexpr int tile_keys() {
+  return FP8 ? ((DQK == 128 && !BS && PSH != 1) ? 192 : 128) : (DQK == 128 ? 96 : 64);
+}
+
+template <bool FP8, int DQK, int DV, int BN_>
 struct Cfg {
   static constexpr int EB = FP8 ? 1 : 2;     // bytes per element
-  // keys per tile.  A phase carries a roughly fixed cost (barriers, the first
-  // operand reads), so larger tiles amortise it; BF16 at d = 128 stops at 96
-  // keys (128 would not fit two waves' registers per SIMD), and BF16 at d = 192
-  // stays at 64 (its 384-byte K rows would not split into whole 1 KB load
-  // blocks per wave at 96)
-  static constexpr int BN = FP8 ? 128 : (DQK == 128 ? 96 : 64);
+  static constexpr int BN = BN_;             // keys per tile
   static constexpr int NBLK = BN / 32;       // 32-key MFMA blocks per tile
   static constexpr int KROW = DQK * EB;      // bytes of one K row
   static constexpr int VROW = DV * EB;       // bytes of one V row
@@ -134,6 +142,15 @@ struct Cfg {
   static constexpr int V_BLOCKS = BN * VCH / 64;
   static constexpr int K_PER_WAVE = K_BLOCKS / kWaves;
   static constexpr int V_PER_WAVE = V_BLOCKS / kWaves;
+  // A wave's consecutive 1 KB load blocks lie kWaves blocks apart.  Where that
+  // is a whole number of rows and a multiple of the swizzle period (16 rows),
+  // every block of a wave has the same in-tile offset pattern, so one per-lane
+  // offset serves all of them and the buffer descriptor moves instead
+  // (K: FP8 and BF16 at d = 128; V: always).
+  static constexpr int K_ROWS_STEP = (kWaves * 64) % KCH == 0 ? kWaves * 64 / KCH : 0;
+  static constexpr int V_ROWS_STEP = (kWaves * 64) % VCH == 0 ? kWaves * 64 / VCH : 0;
+  static constexpr bool K_UNI = K_ROWS_STEP > 0 && K_ROWS_STEP % 16 == 0;
+  static constexpr bool V_UNI = V_ROWS_STEP > 0 && V_ROWS_STEP % 16 == 0;
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
   static constexpr int LDS_BYTES = 2 * V_TILE + 2 * K_TILE;
   // log2-domain growth of the running max tolerated before rescaling, and the
@@ -229,6 +246,22 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
   return r;
 }
 
+// The descriptor of the same buffer moved `delta` bytes on: base + delta and
+// max(size - delta, 0) bytes, so each offset is range-checked exactly as it
+// was against the unmoved descriptor.  On the scalar unit (no vector-written
+// SGPRs, so no wait states are needed before a load reads it).
+__device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t delta) {
+  int w0, w1, w2;
+  asm("s_add_u32 %0, %3, %6\n\t"
+      "s_addc_u32 %1, %4, 0\n\t"
+      "s_sub_i32 %2, %5, %6\n\t"
+      "s_max_i32 %2, %2, 0"
+      : "=&s"(w0), "=&s"(w1), "=&s"(w2)
+      : "s"(r[0]), "s"(r[1]), "s"(r[2]), "s"(delta)
+      : "scc");
+  return i32x4{w0, w1, w2, r[3]};
+}
+
 // Bytes of rows [kb, min(kb + BN, end)) of a tile at pitch `pitch`, on the
 // scalar unit (left to itself the compiler clamps with a vector med3 and a
 // vector multiply, then moves the result back to a scalar register: a chain of
@@ -267,11 +300,23 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // Transposing LDS reads (gfx950).  Within each group of 16 lanes, tr8: lane i
 // byte j = byte (i % 8) of the 8 bytes addressed by lane 2j + i/8; tr16: lane i
 // element j = element (i % 4) of the 4 halves addressed by lane 4j + i/4.
-__device__ __forceinline__ i32x2v lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)p);
+// Operand reads take an LDS byte address.  The K reads' per-lane register
+// already holds the LDS address of the K region, so what is added to it is a
+// compile-time offset below 64 KB that fits the instruction's immediate field
+// (with the region base left in the constant, a 96 KB layout puts the K
+// buffers out of the immediate's reach and every read needs a vector add).
+// The V buffers come first in LDS, so their reads fit as they are.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
 }
-__device__ __forceinline__ i16x4 lds_tr16(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+__device__ __forceinline__ i32x2v lds_tr8(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2v*)(size_t)a);
+}
+__device__ __forceinline__ i16x4 lds_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(size_t)a);
+}
+__device__ __forceinline__ i32x4 lds_load16_at(uint32_t a) {
+  return *(const __attribute__((address_space(3))) i32x4*)(size_t)a;
 }
 
 template <bool FP8>
@@ -291,9 +336,7 @@ struct RowState {
   float m;            // running max, log2 domain
   f32x4 l4;           // the full row sum (every entry)
   f32x16 l16;         // the same, from the all-ones row-sum MFMA (shift per 64-key step)
-  f32x4 rs;           // shift per tile: row sum of the last P.V step's codes (every entry)
-  float lrun;         // shift per tile: the row sum, scaled back step by step
-  float sprev;        // shift per tile: 2^-k of the probabilities in pk
+  float lrun;         // shift per tile: the row sum, each step's part scaled back by its 2^-k
   float kc;           // lean P: integer code offset K = 8 (SHIFT - m) + C0 (m kept on that grid)
 };
 
@@ -333,10 +376,11 @@ template <class C, bool FP8, int DQK, int DV>
 struct Wave {
   static constexpr int NBLK = C::NBLK;
   // per-lane LDS byte offsets (relative to a buffer)
-  int k_lane[C::KG];        // K operand: row l % 32, chunk group position (k-half folded in)
-  int v_lane[DV / 32];      // V^T operand per 32-channel block
-  uint32_t k_dma[C::K_PER_WAVE];
-  uint32_t v_dma[C::V_PER_WAVE];
+  uint32_t k_lane[C::KG];   // K operand: LDS address of K buffer 0 + row l % 32, chunk group position (k-half folded in)
+  uint32_t v_lane[DV / 32]; // V^T operand per 32-channel block: the lane's offset in a V buffer (V buffers lie
+                            // in the first 64 KB of the workgroup's LDS, within reach of the immediate)
+  uint32_t k_dma[C::K_UNI ? 1 : C::K_PER_WAVE];
+  uint32_t v_dma[C::V_UNI ? 1 : C::V_PER_WAVE];
   typename QOp<FP8>::T q[C::QK_STEPS];
   f32x16 s[NBLK];
   uint32_t pk[FP8 ? C::BN / 8 : C::BN / 4];  // this lane's probabilities of the tile (half its keys), MFMA B-operand order
@@ -358,10 +402,15 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   static_assert(!BS || FP8, "block scales are an FP8 feature");
   static_assert(PSH == kShiftNone || FP8, "probability shifts are an FP8 feature");
   constexpr bool PS = PSH == kShiftStep, PT = PSH == kShiftTile;
+  static_assert(kShiftStep == 1, "tile_keys names the per-64-key shift by its value");
+
   static_assert(!LEAN || FP8, "lean-P codes are e4m3 codes");
-  using C = Cfg<FP8, DQK, DV>;
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH>()>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
+  static_assert(!PS || BN == 128, "the per-64-key shift's four max chains cover two 64-key steps");
+  static_assert(!BS || BN == 128, "block-scale exponents are staged one word per 128-key tile");
+  static_assert(C::V_TILE % (16 * kThreads) == 0, "the zero-filled V buffer splits into whole stores");
   uint8_t* const Vs = smem;                 // V buffers 0, 1
   uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
 
@@ -403,7 +452,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   // lane's row l % 32 (the rows of block blk are l % 32 + 32 blk, same swizzle)
 #pragma unroll
   for (int ct = 0; ct < C::KG; ++ct)
-    wv.k_lane[ct] = l32 * C::KROW + 16 * ((ct ^ (hl * (FP8 ? 2 : 1)) ^ k_swizzle<C>(l32)) & (C::KG - 1));
+    wv.k_lane[ct] = lds_addr(Ks) + l32 * C::KROW + 16 * ((ct ^ (hl * (FP8 ? 2 : 1)) ^ k_swizzle<C>(l32)) & (C::KG - 1));
   {
     const int grp16 = lane >> 4, s16 = lane & 15;
     const int lhl = grp16 >> 1, gc = grp16 & 1;
@@ -426,19 +475,29 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
       }
     }
   }
+  // (opaque from here on: the region bases stay in the registers; only the
+  // chunk positions the K reads use, chunks 4kk + {0, 1} (FP8) or 2kk (BF16))
+#pragma unroll
+  for (int ct = 0; ct < C::KG; ++ct) {
+    const bool used = FP8 ? ((ct & 3) < 2 && ct < 4 * C::QK_STEPS) : ((ct & 1) == 0 && ct < 2 * C::QK_STEPS);
+    if (used) asm volatile("" : "+v"(wv.k_lane[ct]));
+  }
   // ---- per-lane global offsets of the tile loads (tile-relative, the same for every tile)
 #pragma unroll
-  for (int i = 0; i < C::K_PER_WAVE; ++i) {
+  for (int i = 0; i < (C::K_UNI ? 1 : C::K_PER_WAVE); ++i) {
     const int blk = w + kWaves * i;
     const int pos = 64 * blk + lane, row = pos / C::KCH, slot = pos % C::KCH;
     wv.k_dma[i] = (uint32_t)row * k_pitch + 16u * k_chunk_pos<C>(row, slot);
   }
 #pragma unroll
-  for (int i = 0; i < C::V_PER_WAVE; ++i) {
+  for (int i = 0; i < (C::V_UNI ? 1 : C::V_PER_WAVE); ++i) {
     const int blk = w + kWaves * i;
     const int pos = 64 * blk + lane, key = pos / C::VCH, slot = pos % C::VCH;
     wv.v_dma[i] = (uint32_t)key * v_pitch + 16u * (slot ^ v_swizzle<FP8>(key));
   }
+  // bytes between a wave's consecutive load blocks, where they share one offset
+  const uint32_t k_blk_bytes = __builtin_amdgcn_readfirstlane(C::K_ROWS_STEP * k_pitch);
+  const uint32_t v_blk_bytes = __builtin_amdgcn_readfirstlane(C::V_ROWS_STEP * v_pitch);
 
   const int kend = min(q0 + kBM, Nq) + off;  // keys visible to the workgroup's last query, plus one
   const int T = (kend + BN - 1) / BN;        // key tiles of the workgroup
@@ -463,7 +522,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 #pragma unroll
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
-      load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
+      if constexpr (C::K_UNI)
+        load_to_lds(i == 0 ? rk : rsrc_advance(rk, i * k_blk_bytes), wv.k_dma[0], Ks + buf * C::K_TILE + 1024 * blk);
+      else
+        load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
     }
   };
   auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
@@ -472,7 +534,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 #pragma unroll
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
-      load_to_lds(rv, wv.v_dma[i], Vs + buf * C::V_TILE + 1024 * blk);
+      if constexpr (C::V_UNI)
+        load_to_lds(i == 0 ? rv : rsrc_advance(rv, i * v_blk_bytes), wv.v_dma[0], Vs + buf * C::V_TILE + 1024 * blk);
+      else
+        load_to_lds(rv, wv.v_dma[i], Vs + buf * C::V_TILE + 1024 * blk);
     }
   };
   // loads of step p: K tile p+1 and V tile p
@@ -508,19 +573,27 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   wv.st.m = -1e30f;
   wv.st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (PS) wv.st.l16 = zero16();
-  if constexpr (PT) {
-    wv.st.rs = f32x4{0.f, 0.f, 0.f, 0.f};
-    wv.st.lrun = 0.f;
-    wv.st.sprev = 1.f;
-  }
+  if constexpr (PT) wv.st.lrun = 0.f;
   wv.st.kc = 0.f;
   // Row-sum selector (A operand of the 16x16 row-sum MFMA): 1.0 where the lane
   // group's parity matches its row group's parity, else 0.  Lane l then finds
   // the sum over the k-step's keys for its own query l % 32 in every entry of
   // its D registers.
-  const bool sel_on = ((lane >> 4) & 1) == (((lane & 15) >> 2) & 1);
-  const int sel_w = sel_on ? (FP8 ? 0x38383838 : 0x3f803f80) : 0;  // e4m3 / bf16 ones
-  const i32x8 sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
+  // The eight operand registers are rebuilt where a step's first row-sum MFMA
+  // needs them, instead of being held through the softmax, where registers are
+  // scarcest: one select against the constant lane mask of the pattern (bit l
+  // set where ((l >> 4) & 1) == ((l >> 2) & 1)), one AND, seven copies.  (The
+  // matrix wave's vector instructions share the SIMD's vector unit with the
+  // other wave's softmax, so the rebuild is kept this short.)
+  auto selector = []() __attribute__((always_inline)) {
+    int w;  // volatile: rebuilt in every step, not hoisted out of the loop
+    asm volatile("v_cndmask_b32_e64 %0, 0, -1, %1\n\tv_and_b32_e32 %0, %2, %0"
+                 : "=v"(w)
+                 : "s"(0xf0f00f0ff0f00f0full), "i"(FP8 ? 0x38383838 : 0x3f803f80));  // e4m3 / bf16 ones
+    return i32x8{w, w, w, w, w, w, w, w};
+  };
+  i32x8 sel;
+  f32x4 rs;  // shift per tile: row sum of one step's codes (every entry), inside a matrix phase
   // With probability block scaling the row sum is a 32x32x64 MFMA against an
   // all-ones A: its B exponents are read per (column, 32-key block) as in the
   // P.V product (the 16x16x128 form reads one column's exponents from the lanes
@@ -547,29 +620,29 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
         const int ks = i / (DV / 32), db = i % (DV / 32);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const i32x2v t = lds_tr8(vb + wv.v_lane[db] + (64 * ks + 32 * (r >> 1) + 16 * (r & 1)) * C::VROW);
+          const i32x2v t = lds_tr8(lds_addr(vb) + wv.v_lane[db] + (64 * ks + 32 * (r >> 1) + 16 * (r & 1)) * C::VROW);
           a[2 * r] = t[0];
           a[2 * r + 1] = t[1];
         }
       } else {
         const int chunk = i / (DV / 32), db = i % (DV / 32);
-        const i16x4 t0 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk) * C::VROW);
-        const i16x4 t1 = lds_tr16(vb + wv.v_lane[db] + (16 * chunk + 8) * C::VROW);
+        const i16x4 t0 = lds_tr16(lds_addr(vb) + wv.v_lane[db] + (16 * chunk) * C::VROW);
+        const i16x4 t1 = lds_tr16(lds_addr(vb) + wv.v_lane[db] + (16 * chunk + 8) * C::VROW);
         const i32x2v u0 = __builtin_bit_cast(i32x2v, t0), u1 = __builtin_bit_cast(i32x2v, t1);
         a = i32x4{u0[0], u0[1], u1[0], u1[1]};
       }
     } else {
       const int j = i - PV_OPS, kk = j / NBLK, blk = j % NBLK;
-      const uint8_t* row = kb + blk * 32 * C::KROW;
+      const uint32_t row = (uint32_t)(kb - Ks) + blk * 32 * C::KROW;  // a compile-time offset
       if constexpr (FP8) {
         // logical chunks 4kk + 2hl + {0, 1}
         const int c0 = 4 * kk, c1 = 4 * kk + 1;
-        const i32x4 lo = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
-        const i32x4 hi = lds_load16(row + wv.k_lane[c1 & (C::KG - 1)] + 16 * (c1 & ~(C::KG - 1)));
+        const i32x4 lo = lds_load16_at(wv.k_lane[c0 & (C::KG - 1)] + row + 16 * (c0 & ~(C::KG - 1)));
+        const i32x4 hi = lds_load16_at(wv.k_lane[c1 & (C::KG - 1)] + row + 16 * (c1 & ~(C::KG - 1)));
         a = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
         const int c0 = 2 * kk;  // logical chunk 2kk + hl
-        a = lds_load16(row + wv.k_lane[c0 & (C::KG - 1)] + 16 * (c0 & ~(C::KG - 1)));
+        a = lds_load16_at(wv.k_lane[c0 & (C::KG - 1)] + row + 16 * (c0 & ~(C::KG - 1)));
       }
     }
     return a;
@@ -588,9 +661,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
           wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
                                 : mfma_fp8_32x32x64_sab<3, 1>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
         } else if constexpr (PT) {
-          // the step's row sum on its own (scaled back on the vector side)
-          if (db == 0)
-            wv.st.rs = mfma_fp8_16x16x128(sel, pb, ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : wv.st.rs);
+          // the step's row sum on its own (scaled back when the phase ends)
+          if (db == 0) rs = mfma_fp8_16x16x128(sel, pb, ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rs);
           wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
                                 : mfma_fp8_32x32x64_sab<3, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
         } else {
@@ -656,11 +728,17 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     // zero-filled or fully loaded V buffer), and at step s_hi the scores of a
     // tile the wave does not need are computed and never read.
     if (pstep >= s_lo && pstep <= s_hi) {
+      sel = selector();
       if constexpr (BS) {
         kexp = ebuf[tile_of(pstep)];
         vexp = ebuf[tile_of(pstep - 1)];
       }
       run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
+      // shift per tile: the row sum of the probabilities just multiplied (they
+      // were 2^k too large; pscale holds the E8M0 exponent of 2^-k, which is
+      // also its fp32 exponent field) joins the running sum.  Its MFMAs were
+      // among the first of the phase, so their result is ready.
+      if constexpr (PT) wv.st.lrun = __builtin_fmaf(rs[0], __uint_as_float(wv.pscale << 23), wv.st.lrun);
     }
   };
 
@@ -695,9 +773,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
     mx = lane_xor32_max(mx);
     const float mt = mx * c;
-    // shift per tile: the row sum of the previous step's probabilities (which
-    // were 2^k too large) joins the running sum before any rescale
-    if constexpr (PT) wv.st.lrun = __builtin_fmaf(wv.st.rs[0], wv.st.sprev, wv.st.lrun);
     if (__any(mt > wv.st.m + C::THRESH)) {  // wave-uniform; rare once the max settles
       float m_new = fmaxf(wv.st.m, mt);
       if constexpr (LEAN) {
@@ -733,9 +808,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
       float kst[NBLK / 2];
       if constexpr (PT) {
         const float kt = fminf(floorf(wv.st.m - mt), 126.f);
-        const uint32_t e = (uint32_t)(127 - (int)kt);  // E8M0 exponent of 2^-k
-        wv.pscale = e;
-        wv.st.sprev = __uint_as_float(e << 23);  // 2^-k
+        wv.pscale = (uint32_t)(127 - (int)kt);  // E8M0 exponent of 2^-k
 #pragma unroll
         for (int ks = 0; ks < NBLK / 2; ++ks) kst[ks] = kt;
       }
@@ -865,7 +938,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   if (grp == 0) barrier(false);
 
   // ---- epilogue: normalise by the row sum and store BF16
-  if constexpr (PT) wv.st.lrun = __builtin_fmaf(wv.st.rs[0], wv.st.sprev, wv.st.lrun);  // the last step's P
   const float lsum = PS ? wv.st.l16[0] : (PT ? wv.st.lrun : wv.st.l4[0]);
   const float inv = sv / lsum;
   if (my_q < Nq) {
@@ -904,7 +976,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // tiles instead of one stream each.
 template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
-  using C = Cfg<FP8, DQK, DV>;
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH>()>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
   const int nqt = (p.Nq + kBM - 1) / kBM;

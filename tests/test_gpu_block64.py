@@ -9,7 +9,8 @@ dimension 192, against the oracle.
   Frobenius error <= 6e-2 and the LSE within the lean-P / FP8-MFMA bound of the
   chunk tests, against the fp64 oracle on the dequantized inputs.
 * With every block scale of a (batch, head) equal to one power of two, the
-  block-scaled kernel must reproduce the per-head kernel bit for bit: a
+  block-scaled kernel must reproduce the per-head kernel bit for bit where
+  both stream tiles of the same size in the same probability mode: a
   power-of-two scale applied inside the MFMA commutes with every rounding.
 * Probability block scaling (``p_block_scale``): the same parity cases, and on
   keys whose block magnitudes differ by 2^+-1 it must cut the error of
@@ -163,8 +164,17 @@ def test_block64_scales_are_applied(require_gpu):
     assert e_b <= TOL["fp8"] and e_h > 0.2 and e_b < 0.25 * e_h, (e_b, e_h)
 
 
-@pytest.mark.parametrize("dqk", [128, 192])
-def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk):
+# (d_qk, probability mode) pairs whose per-head and block-scaled kernels stream
+# tiles of the same size (128 keys; the per-head kernel at d = 128 uses 192-key
+# tiles except with the per-64-key shift)
+SAME_TILES = [(192, m) for m in sorted(miattn.P_MODES)] + [(128, "lean_block"), (128, "exact_block")]
+
+
+@pytest.mark.parametrize("dqk,mode", SAME_TILES)
+def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk, mode):
+    """Every block scale of a head equal to one power of two: the block-scaled
+    kernel gives the per-head kernel's bits (a power-of-two scale inside the
+    MFMA commutes with every rounding), with the same tile size and mode."""
     B, Nq, Nk, Hq, Hkv = 1, 500, 900, 4, 2
     g = np.random.default_rng(dqk)
     codes = [g.integers(0, 256, size=s, dtype=np.uint8) for s in
@@ -177,8 +187,9 @@ def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk)
     nbq, nbk = (Nq + 63) // 64, (Nk + 63) // 64
     blocks = [np.repeat(sq[:, :, None], nbq, 2), np.repeat(sk[:, :, None], nbk, 2), np.repeat(sv[:, :, None], nbk, 2)]
     cdev = [torch.from_numpy(c).cuda() for c in codes]
-    out_h, lse_h = miattn.attn_fwd_chunk(*cdev, *[torch.from_numpy(s).cuda() for s in (sq, sk, sv)])
-    out_b, lse_b = miattn.attn_fwd_block64(*cdev, *[torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in blocks])
+    out_h, lse_h = miattn.attn_fwd_fp8(*cdev, *[torch.from_numpy(s).cuda() for s in (sq, sk, sv)], p_mode=mode)
+    out_b, lse_b = miattn.attn_fwd_fp8(*cdev, *[torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in blocks],
+                                       scales="block64", p_mode=mode)
     torch.cuda.synchronize()
     assert torch.equal(out_h.view(torch.int16), out_b.view(torch.int16))
     assert torch.equal(lse_h.view(torch.int32), lse_b.view(torch.int32))
