@@ -43,11 +43,14 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-chunk] [--no-block64]
        python bench.py --clock-study [--study-seconds S]
 
-``--clock-study`` measures how the input data moves the sustained clock and
-the energy per FLOP: for several input distributions of the 32K workloads it
-runs back-to-back launches for a few seconds while sampling the graphics clock
-and reading the board's energy counter (amdsmi), and prints one JSON line per
-case (time, TFLOP/s, mean SCLK, mean power, TFLOP/J).
+``--clock-study`` measures how the input data and the FP8 probability mode
+move the sustained clock and the energy per FLOP: for several input
+distributions of the 32K workloads (and, on the Gaussian FP8 inputs, every
+probability mode: lean or exact, with no shift, a shift per 128-key tile or
+per 64-key step) it runs back-to-back launches for a few seconds while
+sampling the graphics clock and reading the board's energy counter (amdsmi),
+and prints one JSON line per case (time, TFLOP/s, mean SCLK, mean power,
+TFLOP/J).
 """
 
 from __future__ import annotations
@@ -411,6 +414,10 @@ def clock_study(seconds: float):
         ("flat_q_zero", lambda q, k, v: (torch.zeros_like(q), k, v)),  # all probabilities equal
         ("zero_v", lambda q, k, v: (q, k, torch.zeros_like(v))),
     ]
+    default_mode = miattn.DEFAULT_P_MODE
+    # FP8 probability modes on the Gaussian inputs: lean or exact, no shift,
+    # a shift per 128-key tile, or a shift per 64-key step
+    fp8_modes = [default_mode] + [m for m in sorted(miattn.P_MODES) if m != default_mode]
     for wname in ("fp8_mha_n32k", "bf16_mha_n32k"):
         base = WORKLOADS[wname]
         for cname, fn in cases:
@@ -419,65 +426,74 @@ def clock_study(seconds: float):
             if fn is not None:
                 q, k, v = fn(q, k, v)
             q, k, v = (t.to(torch.bfloat16).to(dev) for t in (q, k, v))
+            out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
             if w.dtype == "fp8":
                 (cq, sq), (ck, sk), (cv, sv) = (miattn.attn_quantize_fp8(t) for t in (q, k, v))
-                args = (cq, ck, cv, sq, sk, sv)
+                modes = fp8_modes if cname == "gaussian" else [default_mode]
             else:
-                args = (q, k, v)
-            out = torch.empty((w.B, w.N, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
-            for _ in range(20):
-                miattn.attn_fwd(*args, out=out)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            miattn.attn_fwd(*args, out=out)
-            e1.record()
-            torch.cuda.synchronize()
-            n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
-            clocks, energy, stop = [], [], threading.Event()
+                modes = [None]
+            for mode in modes:
+                if mode is None:
+                    launch = lambda: miattn.attn_fwd(q, k, v, out=out)  # noqa: E731
+                else:
+                    launch = (lambda m: lambda: miattn.attn_fwd_fp8(cq, ck, cv, sq, sk, sv, out=out,  # noqa: E731
+                                                                      with_lse=False, p_mode=m))(mode)
+                for _ in range(20):
+                    launch()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                launch()
+                e1.record()
+                torch.cuda.synchronize()
+                n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
+                clocks, energy, stop = [], [], threading.Event()
 
-            def sample():
-                while not stop.wait(0.05):
-                    try:
-                        clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-                        energy.append((time.perf_counter(), energy_j()))
-                    except Exception:
-                        pass
+                def sample():
+                    while not stop.wait(0.05):
+                        try:
+                            clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+                            energy.append((time.perf_counter(), energy_j()))
+                        except Exception:
+                            pass
 
-            th = None
-            if handle is not None:
-                th = threading.Thread(target=sample, daemon=True)
-                ej0, t0 = energy_j(), time.perf_counter()
-                th.start()
-            e0.record()
-            for _ in range(n):
-                miattn.attn_fwd(*args, out=out)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / n
-            rec = {"study": "clock_energy", "workload": wname, "inputs": cname, "launches": n,
-                   "ms_per_launch": round(ms, 4), "tflops": round(w.causal_flops / (ms * 1e-3) / 1e12, 1)}
-            if th is not None:
-                t1, ej1 = time.perf_counter(), energy_j()
-                stop.set()
-                th.join()
-                # The energy counter advances in coarse steps (about once a second on
-                # MI355X boards): the rate between its first and last change inside
-                # the window is the board power; the clock reading lags the load, so
-                # only its second half is kept.
-                watts = (ej1 - ej0) / (t1 - t0)
-                steps = [energy[i] for i in range(1, len(energy)) if energy[i][1] != energy[i - 1][1]]
-                rec["energy_steps"] = len(steps)
-                if len(steps) >= 2 and steps[-1][0] > steps[0][0]:
-                    watts = (steps[-1][1] - steps[0][1]) / (steps[-1][0] - steps[0][0])
-                clocks = clocks[len(clocks) // 2:]
-                rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
-                rec["sclk_samples"] = len(clocks)
-                rec["board_watts_mean"] = round(watts, 1)
-                rec["tflop_per_joule"] = round(rec["tflops"] / watts, 3) if watts > 0 else None
-            print(json.dumps(rec), flush=True)
-            del args, out, q, k, v
+                th = None
+                if handle is not None:
+                    th = threading.Thread(target=sample, daemon=True)
+                    ej0, t0 = energy_j(), time.perf_counter()
+                    th.start()
+                e0.record()
+                for _ in range(n):
+                    launch()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / n
+                rec = {"study": "clock_energy", "workload": wname, "inputs": cname, "p_mode": mode or "bf16",
+                       "launches": n, "ms_per_launch": round(ms, 4),
+                       "tflops": round(w.causal_flops / (ms * 1e-3) / 1e12, 1)}
+                if th is not None:
+                    t1, ej1 = time.perf_counter(), energy_j()
+                    stop.set()
+                    th.join()
+                    # The energy counter advances in coarse steps (about once a second on
+                    # MI355X boards): the rate between its first and last change inside
+                    # the window is the board power; the clock reading lags the load, so
+                    # only its second half is kept.
+                    watts = (ej1 - ej0) / (t1 - t0)
+                    steps = [energy[i] for i in range(1, len(energy)) if energy[i][1] != energy[i - 1][1]]
+                    rec["energy_steps"] = len(steps)
+                    if len(steps) >= 2 and steps[-1][0] > steps[0][0]:
+                        watts = (steps[-1][1] - steps[0][1]) / (steps[-1][0] - steps[0][0])
+                    clocks = clocks[len(clocks) // 2:]
+                    rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
+                    rec["sclk_samples"] = len(clocks)
+                    rec["board_watts_mean"] = round(watts, 1)
+                    rec["tflop_per_joule"] = round(rec["tflops"] / watts, 3) if watts > 0 else None
+                print(json.dumps(rec), flush=True)
+            del out, q, k, v
+            if w.dtype == "fp8":
+                del cq, ck, cv, sq, sk, sv
             torch.cuda.empty_cache()
     return 0
 

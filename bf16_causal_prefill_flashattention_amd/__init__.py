@@ -47,6 +47,7 @@ __all__ = [
     "DTYPE_BF16",
     "DTYPE_FP8_E4M3",
     "P_MODES",
+    "DEFAULT_P_MODE",
 ]
 
 DTYPE_BF16 = 0
@@ -56,6 +57,7 @@ SRC_BF16 = 1
 SCALES = {"head": 0, "block64": 1}
 # probability modes of the FP8 kernels (include/miattn.h, MIATTN_P_*)
 P_MODES = {"lean": 0, "lean_block": 1, "exact": 2, "exact_block": 3, "lean_tile": 4, "exact_tile": 5}
+DEFAULT_P_MODE = "lean_tile"  # MIATTN_P_DEFAULT: what attn_fwd and attn_fwd_chunk use on FP8 inputs
 
 _LIB = None
 _HERE = os.path.dirname(os.path.abspath(__file__))

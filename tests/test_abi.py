@@ -42,6 +42,8 @@ def test_probability_mode_constants_match_the_binding():
     for name, code in pkg.P_MODES.items():
         assert header_constant(f"MIATTN_P_{name.upper()}") == code
     assert header_constant("MIATTN_SCALES_HEAD") == 0 and header_constant("MIATTN_SCALES_BLOCK64") == 1
+    m = re.search(r"#define\s+MIATTN_P_DEFAULT\s+MIATTN_P_(\w+)", open(HEADER).read())
+    assert m.group(1).lower() == pkg.DEFAULT_P_MODE
 
 
 def test_every_declared_symbol_is_exported(lib):
