@@ -70,32 +70,144 @@ __device__ __forceinline__ void load8<__bf16>(const __bf16* src, bool valid, flo
   }
 }
 
-// Unnormalised NPT-point Walsh-Hadamard transform of each group of NPT
-// channels of a row held by consecutive lanes, 8 consecutive channels per lane
-// (lane cc holds channels 8cc .. 8cc+7; a group is NPT/8 lanes, aligned in the
-// wave).  Stage widths 1, 2, 4 are inside a lane; widths 8..NPT/2 pair lane cc
-// with lane cc ^ (width / 8).
-template <int NPT>
-__device__ __forceinline__ void fwht_row(float v[8], int cc) {
+// One cross-lane butterfly stage of width DL lanes (DL in {1, 2, 4, 8}, within
+// a 16-lane DPP row): lane l pairs with lane l ^ DL; the lower lane of the pair
+// (bit DL clear) becomes a + b, the upper a - b, where a is the lower lane's
+// value and b the upper's -- the same fp32 operations as the butterfly
+// (b + a = a + b, and a + (-b) = a - b exactly).  DPP reads operands of other
+// lanes inside the vector instruction, so no LDS round trip is needed.
+//   DL = 4, 8: banks (groups of 4 lanes) are wholly lower or upper, so a
+//   bank-masked add (lower banks, reading lane l + DL) and a bank-masked
+//   subtract (upper banks, reading lane l - DL) write the two halves.
+//   DL = 1, 2: lower and upper lanes share banks, so the upper lanes' own value
+//   is negated first (sign-bit XOR, `sgn` = 0x80000000 on upper lanes) and one
+//   quad-permuted add forms partner + own for all lanes.
+// The s_nop 1 gives the two wait states a DPP read needs after the vector
+// write of its source (the compiler does not see into the assembly).
+template <int DL>
+__device__ __forceinline__ void fwht_xlane(float v[8], uint32_t sgn) {
+  float r[8];
+  if constexpr (DL == 4 || DL == 8) {
+#define MIATTN_BFLY(LO, HI)                                                     \
+  "v_add_f32_dpp %" #LO ", %" #HI ", %" #HI " row_shl:" DLS " row_mask:0xf bank_mask:" LOB "\n\t" \
+  "v_sub_f32_dpp %" #LO ", %" #HI ", %" #HI " row_shr:" DLS " row_mask:0xf bank_mask:" HIB "\n\t"
+    if constexpr (DL == 4) {
+#define DLS "4"
+#define LOB "0x5"
+#define HIB "0xa"
+      asm("s_nop 1\n\t" MIATTN_BFLY(0, 8) MIATTN_BFLY(1, 9) MIATTN_BFLY(2, 10) MIATTN_BFLY(3, 11)
+              MIATTN_BFLY(4, 12) MIATTN_BFLY(5, 13) MIATTN_BFLY(6, 14) MIATTN_BFLY(7, 15)
+          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+          : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+#undef DLS
+#undef LOB
+#undef HIB
+    } else {
+#define DLS "8"
+#define LOB "0x3"
+#define HIB "0xc"
+      asm("s_nop 1\n\t" MIATTN_BFLY(0, 8) MIATTN_BFLY(1, 9) MIATTN_BFLY(2, 10) MIATTN_BFLY(3, 11)
+              MIATTN_BFLY(4, 12) MIATTN_BFLY(5, 13) MIATTN_BFLY(6, 14) MIATTN_BFLY(7, 15)
+          : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+          : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+#undef DLS
+#undef LOB
+#undef HIB
+    }
+#undef MIATTN_BFLY
+  } else {
+    float t[8];
 #pragma unroll
-  for (int wd = 1; wd < 8; wd <<= 1) {
+    for (int i = 0; i < 8; ++i) t[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ sgn);
+#define MIATTN_QADD(R, S, T) "v_add_f32_dpp %" #R ", %" #S ", %" #T " quad_perm:" QP " row_mask:0xf bank_mask:0xf\n\t"
+#define MIATTN_QSTAGE                                                                                            \
+  asm("s_nop 1\n\t" MIATTN_QADD(0, 8, 16) MIATTN_QADD(1, 9, 17) MIATTN_QADD(2, 10, 18) MIATTN_QADD(3, 11, 19)      \
+          MIATTN_QADD(4, 12, 20) MIATTN_QADD(5, 13, 21) MIATTN_QADD(6, 14, 22) MIATTN_QADD(7, 15, 23)            \
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]) \
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(t[0]),    \
+        "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]), "v"(t[7]))
+    if constexpr (DL == 1) {
+#define QP "[1,0,3,2]"
+      MIATTN_QSTAGE;
+#undef QP
+    } else {
+#define QP "[2,3,0,1]"
+      MIATTN_QSTAGE;
+#undef QP
+    }
+#undef MIATTN_QSTAGE
+#undef MIATTN_QADD
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (!(i & wd)) {
-        const float a = v[i], b = v[i + wd];
-        v[i] = a + b;
-        v[i + wd] = a - b;
+  for (int i = 0; i < 8; ++i) v[i] = r[i];
+}
+
+// Row layout of the quantizer kernels: TPR lanes per row; lane c (0..TPR-1)
+// holds, for each i < NI, the 8 consecutive channels 8 (TPR i + c) .. +7 in
+// v[i][0..7], so each of a row's NI loads reads contiguous bytes over its TPR
+// lanes.  Without the rotation a lane holds one group (TPR = D / 8: a load
+// instruction covers whole rows); with it, 4 lanes per row (NI = D / 32), so
+// that all but two butterfly stages run inside a lane.
+template <int D, bool HAD>
+struct Row {
+  static constexpr int TPR = HAD ? 4 : D / 8;  // lanes per row
+  static constexpr int NI = D / (8 * TPR);     // 8-channel groups per lane
+  static constexpr int RPP = kQThreads / TPR;  // rows per pass of a workgroup
+  static __device__ __forceinline__ int ch(int c, int i) { return 8 * (TPR * i + c); }
+};
+
+// Butterfly stage of width 32 or 64 channels, inside a lane: groups i and
+// i + G (G = 1 or 2, i with bit G clear) -> (a + b, a - b).
+template <int NI, int G>
+__device__ __forceinline__ void fwht_groups(float (&v)[NI][8]) {
+  static_assert(NI % (2 * G) == 0, "groups pair up");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (!(i & G)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = v[i][j], b = v[i + G][j];
+        v[i][j] = a + b;
+        v[i + G][j] = a - b;
+      }
+    }
+  }
+}
+
+// Unnormalised Walsh-Hadamard transform of each row (4 lanes per row): one
+// H_128 at D = 128,
+// H_64 on each of the three groups of 64 channels at D = 192, as butterfly
+// stages of widths 1, 2, 4 (inside each 8-channel group), 8 and 16 (lane c
+// with c ^ 1, c ^ 2), 32 (groups i, i ^ 1) and, at D = 128, 64 (groups i,
+// i ^ 2).  With LAST = false the final stage is left out (see amax_kernel).
+// sgn1 / sgn2: 0x80000000 on lanes whose bit 0 / bit 1 is set, else 0.
+template <int D, bool LAST>
+__device__ __forceinline__ void fwht_row(float (&v)[D / 32][8], uint32_t sgn1, uint32_t sgn2) {
+  constexpr int NI = D / 32;
+  static_assert(Row<D, true>::NI == NI, "4 lanes per row");
+#pragma unroll
+  for (int g = 0; g < NI; ++g) {
+#pragma unroll
+    for (int wd = 1; wd < 8; wd <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (!(i & wd)) {
+          const float a = v[g][i], b = v[g][i + wd];
+          v[g][i] = a + b;
+          v[g][i + wd] = a - b;
+        }
       }
     }
   }
 #pragma unroll
-  for (int dl = 1; dl < NPT / 8; dl <<= 1) {
-    const bool upper = (cc & dl) != 0;
+  for (int g = 0; g < NI; ++g) fwht_xlane<1>(v[g], sgn1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float o = __shfl_xor(v[i], dl, kWave);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
-    }
+  for (int g = 0; g < NI; ++g) fwht_xlane<2>(v[g], sgn2);
+  if constexpr (D == 128) {
+    fwht_groups<NI, 1>(v);
+    if constexpr (LAST) fwht_groups<NI, 2>(v);
+  } else {
+    if constexpr (LAST) fwht_groups<NI, 1>(v);
   }
 }
 
@@ -105,26 +217,47 @@ __global__ void amax_init_kernel(uint32_t* amax_bits, int n) {
 }
 
 // Grid: one workgroup per (b*H + h, chunk of kRowsPerBlock sequence rows).
+// With the rotation the last butterfly stage is not formed: the larger
+// magnitude of its two outputs, max(|a + b|, |a - b|), equals |a| + |b|, and
+// in fp32 max(|fl(a + b)|, |fl(a - b)|) = fl(|a| + |b|) exactly (one of the two
+// is +-(|a| + |b|) before rounding, the other no larger, and round-to-nearest
+// is monotone and symmetric), so the amax is the same bits.
 template <typename T, int D, bool HAD>
 __global__ __launch_bounds__(kQThreads) void amax_kernel(const T* x, uint32_t* amax_bits, int N, int H,
                                                          int nchunks) {
-  constexpr int TPR = D / 8;              // threads per row
-  constexpr int RPP = kQThreads / TPR;    // rows per pass
+  using L = Row<D, HAD>;
+  constexpr int TPR = L::TPR, RPP = L::RPP, NI = L::NI;
   const int bh = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, rr = tid / TPR, cc = tid % TPR;
-  const bool active = rr < RPP;
+  const uint32_t sgn1 = (tid & 1) ? 0x80000000u : 0u, sgn2 = (tid & 2) ? 0x80000000u : 0u;
+  const bool active = rr < RPP;  // D = 192 without the rotation: 240 of the 256 lanes
   const int r0 = chunk * kRowsPerBlock;
   const int r1 = min(r0 + kRowsPerBlock, N);
   float m = 0.f;
   for (int base = r0; base < r1; base += RPP) {  // uniform trip count over the block
     const int r = base + rr;
     const bool valid = active && r < r1;
-    float v[8];
-    load8<T>(x + (((size_t)b * N + (valid ? r : 0)) * H + h) * D + cc * 8, valid, v);
-    if constexpr (HAD) fwht_row<(D == 128 ? 128 : 64)>(v, cc);
+    const T* row = x + (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
+    float v[NI][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int i = 0; i < NI; ++i) load8<T>(row + L::ch(cc, i), valid, v[i]);
+    if constexpr (HAD) {
+      fwht_row<D, false>(v, sgn1, sgn2);
+      constexpr int G = D == 128 ? 2 : 1;  // the last stage pairs groups i and i + G
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (!(i & G)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]) + fabsf(v[i + G][j]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
@@ -142,11 +275,12 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const T* x, uint32_t* a
 template <typename T, int D, bool HAD>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const T* x, uint8_t* y, const uint32_t* amax_bits,
                                                              int N, int H, int nchunks) {
-  constexpr int TPR = D / 8;
-  constexpr int RPP = kQThreads / TPR;
+  using L = Row<D, HAD>;
+  constexpr int TPR = L::TPR, RPP = L::RPP, NI = L::NI;
   const int bh = blockIdx.x / nchunks, chunk = blockIdx.x % nchunks;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, rr = tid / TPR, cc = tid % TPR;
+  const uint32_t sgn1 = (tid & 1) ? 0x80000000u : 0u, sgn2 = (tid & 2) ? 0x80000000u : 0u;
   const bool active = rr < RPP;
   const float amax = __builtin_bit_cast(float, amax_bits[bh]);
   const float inv = amax == 0.f ? 1.f : 448.f / amax;
@@ -155,15 +289,20 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const T* x, uint8_t
   for (int base = r0; base < r1; base += RPP) {
     const int r = base + rr;
     const bool valid = active && r < r1;
-    const size_t off = (((size_t)b * N + (valid ? r : 0)) * H + h) * D + cc * 8;
-    float v[8];
-    load8<T>(x + off, valid, v);
-    if constexpr (HAD) fwht_row<(D == 128 ? 128 : 64)>(v, cc);
+    const size_t off = (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
+    float v[NI][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
-    if (valid) {
-      i32x2 codes = {(int)pack_fp8x4(v[0], v[1], v[2], v[3]), (int)pack_fp8x4(v[4], v[5], v[6], v[7])};
-      *reinterpret_cast<i32x2*>(y + off) = codes;
+    for (int i = 0; i < NI; ++i) load8<T>(x + off + L::ch(cc, i), valid, v[i]);
+    if constexpr (HAD) fwht_row<D, true>(v, sgn1, sgn2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = fminf(fmaxf(v[i][j] * inv, -448.f), 448.f);
+      if (valid) {
+        i32x2 codes = {(int)pack_fp8x4(v[i][0], v[i][1], v[i][2], v[i][3]),
+                       (int)pack_fp8x4(v[i][4], v[i][5], v[i][6], v[i][7])};
+        *reinterpret_cast<i32x2*>(y + off + L::ch(cc, i)) = codes;
+      }
     }
   }
 }
@@ -191,35 +330,43 @@ __device__ __forceinline__ int block_exponent(float amax) {
 }
 
 // One workgroup per (b*H + h, 64-position block): the block is read once into
-// registers, its amax reduced in the workgroup, then quantized and written.
+// registers (PASSES passes of RPP rows), its amax reduced in the workgroup,
+// then quantized and written.
 template <typename T, int D, bool HAD>
 __global__ __launch_bounds__(kQThreads) void quantize_block64_kernel(const T* x, uint8_t* y, float* scale, int N,
                                                                      int H, int nblk) {
-  constexpr int TPR = D / 8;                      // threads per row
-  constexpr int RPP = kQThreads / TPR;            // rows per pass
-  constexpr int PASSES = (64 + RPP - 1) / RPP;    // passes over the 64 rows
+  using L = Row<D, HAD>;
+  constexpr int TPR = L::TPR, RPP = L::RPP, NI = L::NI;
+  constexpr int PASSES = (64 + RPP - 1) / RPP;
   const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, rr = tid / TPR, cc = tid % TPR;
+  const uint32_t sgn1 = (tid & 1) ? 0x80000000u : 0u, sgn2 = (tid & 2) ? 0x80000000u : 0u;
   const int r0 = blk * 64, r1 = min(r0 + 64, N);
-  float v[PASSES][8];
+  float v[PASSES][NI][8];
   float m = 0.f;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int r = r0 + ps * RPP + rr;
     const bool valid = rr < RPP && ps * RPP + rr < 64 && r < r1;
-    load8<T>(x + (((size_t)b * N + (valid ? r : 0)) * H + h) * D + cc * 8, valid, v[ps]);
+    const size_t off = (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load8<T>(x + off + L::ch(cc, i), valid, v[ps][i]);
     if constexpr (HAD) {
-      fwht_row<(D == 128 ? 128 : 64)>(v[ps], cc);
+      fwht_row<D, true>(v[ps], sgn1, sgn2);
       const float norm = D == 128 ? kInvSqrt128 : 0.125f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[ps][i] = v[ps][i] * norm;
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[ps][i][j] = v[ps][i][j] * norm;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[ps][i]));
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[ps][i][j]));
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
   __shared__ float wmax[kQThreads / kWave];
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
   __syncthreads();
@@ -234,12 +381,15 @@ __global__ __launch_bounds__(kQThreads) void quantize_block64_kernel(const T* x,
   for (int ps = 0; ps < PASSES; ++ps) {
     const int r = r0 + ps * RPP + rr;
     const bool valid = rr < RPP && ps * RPP + rr < 64 && r < r1;
-    float w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = v[ps][i] * inv;  // exact: |w| <= 448
-    if (valid) {
-      i32x2 codes = {(int)pack_fp8x4(w[0], w[1], w[2], w[3]), (int)pack_fp8x4(w[4], w[5], w[6], w[7])};
-      *reinterpret_cast<i32x2*>(y + (((size_t)b * N + r) * H + h) * D + cc * 8) = codes;
+    for (int i = 0; i < NI; ++i) {
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = v[ps][i][j] * inv;  // exact: |w| <= 448
+      if (valid) {
+        i32x2 codes = {(int)pack_fp8x4(w[0], w[1], w[2], w[3]), (int)pack_fp8x4(w[4], w[5], w[6], w[7])};
+        *reinterpret_cast<i32x2*>(y + (((size_t)b * N + r) * H + h) * D + L::ch(cc, i)) = codes;
+      }
     }
   }
 }
