@@ -19,6 +19,14 @@ Entry points (same names as the C ABI):
 * ``attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None,
   with_lse=True, softmax_scale=None, scales="head", p_mode="lean")`` (FP8
   with a chosen scale granularity and probability mode, ``P_MODES``)
+* ``attn_fwd_ws_size(B, Hq, Hkv, Nq, Nk, d_qk, d_v, fp8, scales="head",
+  p_mode=DEFAULT_P_MODE, device=None)`` and ``attn_fwd_ws(q, k, v, q_scale=None,
+  k_scale=None, v_scale=None, out=None, lse=None, with_lse=True,
+  softmax_scale=None, scales="head", p_mode=DEFAULT_P_MODE, workspace=None)``
+  (BF16 or FP8 with a workspace, which lets launches that leave compute units
+  idle split their keys; the workspace is allocated here when not given), and
+  ``attn_fwd_ws_bind(...)``, which checks and marshals such a call once and
+  returns a callable that enqueues it again
 * ``attn_status_string(status)``, ``attn_version()``
 
 and ``flash_attn_func``, a ``flash_attn_func``-style drop-in over them (BSHD
@@ -36,6 +44,9 @@ __all__ = [
     "attn_fwd_block64",
     "attn_fwd_chunk",
     "attn_fwd_fp8",
+    "attn_fwd_ws",
+    "attn_fwd_ws_bind",
+    "attn_fwd_ws_size",
     "attn_quantize_fp8",
     "attn_quantize_fp8_block64",
     "attn_status_string",
@@ -100,6 +111,12 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_fp8.restype = ci
     lib.attn_quantize_fp8_block64.argtypes = [vp, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8_block64.restype = ci
+    sz = ctypes.c_size_t
+    lib.attn_fwd_ws_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
+    lib.attn_fwd_ws_size.restype = ci
+    lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, ci,
+                                ci, vp, sz, vp]
+    lib.attn_fwd_ws.restype = ci
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -308,6 +325,86 @@ def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out=None, lse=None, with_ls
     return out, lse
 
 
+_WS_SIZES = {}  # (device index, arguments) -> attn_fwd_ws_size bytes
+
+
+def attn_fwd_ws_size(B, Hq, Hkv, Nq, Nk, d_qk, d_v, fp8, scales="head", p_mode=DEFAULT_P_MODE, device=None) -> int:
+    """Workspace bytes ``attn_fwd_ws`` needs for these sizes on ``device`` (the
+    current GPU by default); 0 when the launch does not split its keys."""
+    torch = _torch()
+    if scales not in SCALES:
+        raise ValueError(f"scales must be one of {sorted(SCALES)}")
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {sorted(P_MODES)}")
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    key = (idx, B, Hq, Hkv, Nq, Nk, d_qk, d_v, bool(fp8), scales, p_mode)
+    n = _WS_SIZES.get(key)
+    if n is None:
+        c = ctypes.c_size_t(0)
+        with torch.cuda.device(idx):  # the figure depends on the device's compute units
+            st = load_library().attn_fwd_ws_size(B, Hq, Hkv, Nq, Nk, d_qk, d_v,
+                                                 DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16, SCALES[scales],
+                                                 P_MODES[p_mode], ctypes.byref(c))
+        if st != 0:
+            raise MiattnError("attn_fwd_ws_size", st)
+        n = _WS_SIZES[key] = int(c.value)
+    return n
+
+
+def attn_fwd_ws_bind(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None, lse=None, with_lse=True,
+                     softmax_scale=None, scales="head", p_mode=DEFAULT_P_MODE, workspace=None):
+    """Check and marshal an ``attn_fwd_ws`` call once.  Returns ``(call, out,
+    lse)``: ``call()`` enqueues the call on the stream that was current here,
+    with these tensors (for loops over fixed buffers; the tensors must stay
+    alive).  Arguments as ``attn_fwd_ws``."""
+    torch = _torch()
+    if scales not in SCALES:
+        raise ValueError(f"scales must be one of {sorted(SCALES)}")
+    if p_mode not in P_MODES:
+        raise ValueError(f"p_mode must be one of {sorted(P_MODES)}")
+    block64 = scales == "block64" and q.dtype != torch.bfloat16
+    q, k, v, dtype, ptr_s, (B, Nq, Nk, Hq, Hkv, dqk, dv) = _attn_args(q, k, v, q_scale, k_scale, v_scale, block64)
+    out = _out_tensor(out, q, B, Nq, Hq, dv)
+    lse = _lse_tensor(lse, with_lse, q, B, Hq, Nq)
+    need = attn_fwd_ws_size(B, Hq, Hkv, Nq, Nk, dqk, dv, dtype == DTYPE_FP8_E4M3, scales, p_mode, q.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_gpu_contig("workspace", workspace)
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on the device of q")
+    argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+            B, Hq, Hkv, Nq, Nk, dqk, dv, dtype, ptr_s[0], ptr_s[1], ptr_s[2],
+            0.0 if softmax_scale is None else float(softmax_scale), SCALES[scales], P_MODES[p_mode],
+            None if workspace is None else workspace.data_ptr(),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    fn = load_library().attn_fwd_ws
+    keep = (q, k, v, out, lse, workspace)  # noqa: F841  (held by the closure)
+
+    def call():
+        st = fn(*argv)
+        if st != 0:
+            raise MiattnError("attn_fwd_ws", st)
+        return keep
+
+    return call, out, lse
+
+
+def attn_fwd_ws(q, k, v, q_scale=None, k_scale=None, v_scale=None, out=None, lse=None, with_lse=True,
+                softmax_scale=None, scales="head", p_mode=DEFAULT_P_MODE, workspace=None):
+    """Causal attention through ``attn_fwd_ws``: BF16 tensors as
+    ``attn_fwd_chunk`` (``scales`` and ``p_mode`` unused), e4m3 codes as
+    ``attn_fwd_fp8``.  A launch whose query tiles leave compute units idle
+    splits its keys over them, with partial results in ``workspace`` (a uint8
+    GPU tensor of at least ``attn_fwd_ws_size`` bytes; allocated here when
+    None).  Returns ``(out, lse)`` as ``attn_fwd_chunk``."""
+    call, out, lse = attn_fwd_ws_bind(q, k, v, q_scale, k_scale, v_scale, out, lse, with_lse, softmax_scale, scales,
+                                      p_mode, workspace)
+    call()
+    return out, lse
+
+
 def _quantize(fn_name, x, hadamard, out, scale, scale_shape):
     torch = _torch()
     _check_gpu_contig("x", x)
@@ -375,21 +472,20 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=True, ret
         raise ValueError('fp8_scales must be "head" or "block64"')
     if p_block_scale and not (fp8 and fp8_scales == "block64"):
         raise ValueError('p_block_scale needs fp8=True and fp8_scales="block64"')
+    p_mode = DEFAULT_P_MODE
     if fp8 and fp8_scales == "block64":
         (cq, sq) = attn_quantize_fp8_block64(q.contiguous(), hadamard=hadamard)
         (ck, sk) = attn_quantize_fp8_block64(k.contiguous(), hadamard=hadamard)
         (cv, sv) = attn_quantize_fp8_block64(v.contiguous())
-        out, lse = attn_fwd_block64(cq, ck, cv, sq, sk, sv, with_lse=return_lse, softmax_scale=softmax_scale,
-                                    p_block_scale=p_block_scale)
-        return (out, lse) if return_lse else out
-    if fp8:
+        args = (cq, ck, cv, sq, sk, sv)
+        p_mode = "lean_block" if p_block_scale else "lean"  # as attn_fwd_block64
+    elif fp8:
         (cq, sq) = attn_quantize_fp8(q.contiguous(), hadamard=hadamard)
         (ck, sk) = attn_quantize_fp8(k.contiguous(), hadamard=hadamard)
         (cv, sv) = attn_quantize_fp8(v.contiguous())
         args = (cq, ck, cv, sq, sk, sv)
     else:
         args = (q.contiguous(), k.contiguous(), v.contiguous())
-    if q.shape[1] == k.shape[1] and softmax_scale is None and not return_lse:
-        return attn_fwd(*args)
-    out, lse = attn_fwd_chunk(*args, with_lse=return_lse, softmax_scale=softmax_scale)
+    out, lse = attn_fwd_ws(*args, with_lse=return_lse, softmax_scale=softmax_scale,
+                           scales=fp8_scales if fp8 else "head", p_mode=p_mode)
     return (out, lse) if return_lse else out

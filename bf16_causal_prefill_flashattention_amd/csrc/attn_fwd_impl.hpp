@@ -109,7 +109,7 @@ namespace {
 
 constexpr int kThreads = 512;  // 8 waves, two per SIMD
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
+constexpr int kBM = kQueryTile;  // queries per workgroup (8 waves x 32)
 
 // Keys per tile.  A phase carries a roughly fixed cost (barriers, the first
 // operand reads), so larger tiles amortise it.  FP8 at d = 128 with one scale
@@ -121,7 +121,7 @@ constexpr int kBM = 256;  // queries per workgroup (8 waves x 32)
 // at 64 (its 384-byte K rows would not split into whole blocks at 96).
 template <bool FP8, int DQK, bool BS, int PSH>
 constexpr int tile_keys() {
-  return FP8 ? ((DQK == 128 && !BS && PSH != 1) ? 192 : 128) : (DQK == 128 ? 96 : 64);
+  return tile_keys_of(FP8, DQK, BS, PSH == 1);
 }
 
 template <bool FP8, int DQK, int DV, int BN_>
@@ -396,9 +396,9 @@ struct Wave {
 // key order; the order only decides which tiles the workgroups of an XCD read
 // at the same time).  Called by every thread of the workgroup; leaves no load
 // in flight and no wave reading LDS when it returns.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN>
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT>
 __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
-                                          bool rev) {
+                                          bool rev, int ta, int tb, int slot) {
   static_assert(!BS || FP8, "block scales are an FP8 feature");
   static_assert(PSH == kShiftNone || FP8, "probability shifts are an FP8 feature");
   constexpr bool PS = PSH == kShiftStep, PT = PSH == kShiftTile;
@@ -500,13 +500,21 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   const uint32_t v_blk_bytes = __builtin_amdgcn_readfirstlane(C::V_ROWS_STEP * v_pitch);
 
   const int kend = min(q0 + kBM, Nq) + off;  // keys visible to the workgroup's last query, plus one
-  const int T = (kend + BN - 1) / BN;        // key tiles of the workgroup
+  // key tiles of the item: [ta, T), a key range of the query tile (key split) or
+  // all of it (ta = 0).  (Without the split the expressions below are kept
+  // free of the range: the unsplit kernel's register allocation is sensitive
+  // to them.)
+  const int T = SPLIT ? min((kend + BN - 1) / BN, tb) : (kend + BN - 1) / BN;
+  const int NT = SPLIT ? T - ta : T;  // steps 0..NT (step NT only drains the last P.V product)
   // tiles this wave needs: keys up to the position of its last valid query
-  const int Tw = qw0 < Nq ? ((min(qw0 + 31, Nq - 1) + off) / BN + 1) : 0;
+  const int Tw = qw0 < Nq ? (SPLIT ? max(0, min((min(qw0 + 31, Nq - 1) + off) / BN + 1, T) - ta)
+                                   : ((min(qw0 + 31, Nq - 1) + off) / BN + 1))
+                          : 0;
   // steps [s_lo, s_hi) carry the wave's tiles; step s visits tile tile_of(s),
-  // and steps at or beyond T map to tile T (an empty load range)
-  const int s_lo = rev ? T - Tw : 0, s_hi = rev ? T : Tw;
-  const int t_base = rev ? T - 1 : 0, t_dir = rev ? -1 : 1;
+  // and steps at or beyond NT map to tile T (an empty load range).  A reversed
+  // walk covers a whole query tile.
+  const int s_lo = rev ? NT - Tw : 0, s_hi = rev ? NT : Tw;
+  const int t_base = rev ? T - 1 : (SPLIT ? ta : 0), t_dir = rev ? -1 : 1;
   // (unsigned min: the -1 of a downward walk past tile 0 also maps to T)
   auto tile_of = [&](int s) __attribute__((always_inline)) {
     return (int)min((uint32_t)(t_base + t_dir * s), (uint32_t)T);
@@ -921,14 +929,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     barrier(!GA);
     if (GA && !FP8) issue_step(ps);
     vector_work(ps);
-    if (!GA && ps + 1 <= T) issue_step(ps + 1);
+    if (!GA && ps + 1 <= NT) issue_step(ps + 1);
     barrier(GA);
   };
   // one loop per group, so the group decisions inside a step are compile-time
   auto run_steps = [&](auto group) __attribute__((always_inline)) {
-    for (int ps = 0; ps <= T; ps += 2) {
+    for (int ps = 0; ps <= NT; ps += 2) {
       step(ps, std::integral_constant<int, 0>{}, group);
-      if (ps + 1 <= T) step(ps + 1, std::integral_constant<int, 1>{}, group);
+      if (ps + 1 <= NT) step(ps + 1, std::integral_constant<int, 1>{}, group);
     }
   };
   if (grp == 0)
@@ -939,6 +947,28 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 
   // ---- epilogue: normalise by the row sum and store BF16
   const float lsum = PS ? wv.st.l16[0] : (PT ? wv.st.lrun : wv.st.l4[0]);
+  if (SPLIT && slot >= 0) {
+    // one key range of a split query tile: the rows normalised over the range,
+    // in fp32, and the range's log2 sum of exp, for the merge.  A row that sees
+    // no key of the range (its position lies before the range) has lsum = 0:
+    // output 0 and sum -inf, a weight of 0 in the merge.
+    if (my_q < Nq) {
+      const bool seen = lsum > 0.f;
+      const float inv = seen ? sv / lsum : 0.f;
+      const size_t row = (size_t)slot * kBM + (my_q - q0);
+      if (hl == 0) p.ws_lse[row] = seen ? wv.st.m - C::SHIFT + __log2f(lsum) : -INFINITY;
+      float* wo = p.ws_o + row * DV;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o4 = {wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv, wv.st.o[d][4 * i + 2] * inv,
+                            wv.st.o[d][4 * i + 3] * inv};
+          *reinterpret_cast<f32x4*>(wo + d * 32 + 8 * i + 4 * hl) = o4;
+        }
+    }
+    return;
+  }
   const float inv = sv / lsum;
   if (my_q < Nq) {
     // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
@@ -974,7 +1004,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
 // tiles instead of one stream each.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN>
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH>()>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
@@ -982,24 +1012,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   const int nqt = (p.Nq + kBM - 1) / kBM;
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
-  const bool single = (long long)nbh * nqt <= G;  // one tile per unit
-  const int per_bh = single ? nqt : (nqt + 1) / 2;  // units per (batch, head)
   const bool by_xcd = (nbh % 8 == 0) && (G % 8 == 0);
-  const int rank = by_xcd ? wg / 8 : wg, nrank = by_xcd ? G / 8 : G;
-  const int nunit = by_xcd ? (nbh / 8) * per_bh : nbh * per_bh;
-  // one call site (the item body is large): the two tiles of a unit are
-  // iterations half = 0 (the later, heavier tile) and half = 1
-  int u = rank, half = 0;
-  while (u < nunit) {
-    const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
-    const int j = u % per_bh;
-    const int qt = half == 0 ? nqt - 1 - j : j;
-    if (half == 0 || j != nqt - 1 - j) attn_item<DQK, DV, FP8, BS, PSH, LEAN>(p, smem, ebuf, bh, qt, !single && half == 1);
-    if (single) {
-      u += nrank;
-    } else {
-      u += half * nrank;
-      half ^= 1;
+  if constexpr (SPLIT) {
+    // key split: one workgroup per key range, B * Hq * split_units of them; the
+    // ranges of a (batch, head) are its query tiles' ranges in order
+    const int L = p.split_tiles, per_bh = p.split_units;
+    const int bh = by_xcd ? 8 * ((wg / 8) / per_bh) + wg % 8 : wg / per_bh;
+    const int j = (by_xcd ? wg / 8 : wg) % per_bh;
+    int qt = 0, r = j;
+    for (; qt < nqt - 1; ++qt) {
+      const int nr = (qtile_key_tiles(qt, p.Nq, p.Nk, C::BN) + L - 1) / L;
+      if (r < nr) break;
+      r -= nr;
+    }
+    const bool multi = (qtile_key_tiles(qt, p.Nq, p.Nk, C::BN) + L - 1) / L > 1;
+    attn_item<DQK, DV, FP8, BS, PSH, LEAN, true>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
+                                                 multi ? bh * per_bh + j : -1);
+  } else {
+    const bool single = (long long)nbh * nqt <= G;  // one tile per unit
+    const int per_bh = single ? nqt : (nqt + 1) / 2;  // units per (batch, head)
+    const int rank = by_xcd ? wg / 8 : wg, nrank = by_xcd ? G / 8 : G;
+    const int nunit = by_xcd ? (nbh / 8) * per_bh : nbh * per_bh;
+    // one call site (the item body is large): the two tiles of a unit are
+    // iterations half = 0 (the later, heavier tile) and half = 1
+    int u = rank, half = 0;
+    while (u < nunit) {
+      const int bh = by_xcd ? 8 * (u / per_bh) + wg % 8 : u / per_bh;
+      const int j = u % per_bh;
+      const int qt = half == 0 ? nqt - 1 - j : j;
+      if (half == 0 || j != nqt - 1 - j)
+        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false>(p, smem, ebuf, bh, qt, !single && half == 1, 0, 0, -1);
+      if (single) {
+        u += nrank;
+      } else {
+        u += half * nrank;
+        half ^= 1;
+      }
     }
   }
 }
@@ -1007,7 +1055,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
 // Launch one variant (d_v = 128) on `grid` persistent workgroups.
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN>
 hipError_t launch_attn_variant(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN>), grid, dim3(kThreads), 0, stream, p);
+  if (p.split_tiles > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -29,7 +29,44 @@ struct AttnParams {
   // FP8 probability mode (PMode): how the probabilities are rounded to e4m3
   // for the P.V product
   int p_mode;
+  // Key split (split_tiles > 0, chosen by attn_split_plan): query tile qt of a
+  // (batch, head) is cut into ceil(T / split_tiles) work items over consecutive
+  // ranges of split_tiles key tiles (T = the key tiles it needs); the
+  // split_units items of a (batch, head) are its query tiles' ranges in order.
+  // Items of a query tile with more than one range write their output rows
+  // normalised, in fp32, to ws_o [B*Hq*split_units, kQueryTile, d_v] and their
+  // log2-domain sums of exp to ws_lse [B*Hq*split_units, kQueryTile] (slot
+  // bh * split_units + item), and attn_merge_kernel combines the ranges.
+  int split_tiles;
+  int split_units;
+  float* ws_o;
+  float* ws_lse;
 };
+
+// Queries per work item (one workgroup of 8 waves x 32 queries).
+constexpr int kQueryTile = 256;
+
+// Keys per tile of a kernel variant: FP8 at d_qk = 128 with one scale per head
+// and no per-64-key probability shift streams 192-key tiles, the other FP8
+// variants 128; BF16 96 at d_qk = 128 and 64 at d_qk = 192.
+constexpr int tile_keys_of(bool fp8, int d_qk, bool block64, bool shift_step) {
+  return fp8 ? ((d_qk == 128 && !block64 && !shift_step) ? 192 : 128) : (d_qk == 128 ? 96 : 64);
+}
+
+// Key tiles query tile qt needs: keys up to the position of its last query.
+__host__ __device__ inline int qtile_key_tiles(int qt, int Nq, int Nk, int bn) {
+  const long long last = (long long)(qt + 1) * kQueryTile < Nq ? (long long)(qt + 1) * kQueryTile : Nq;
+  return (int)((last + (Nk - Nq) - 1) / bn + 1);
+}
+
+// Key split of one launch on the current device: tiles = key tiles per work
+// item (0: no split), units = work items per (batch, head), bytes = workspace,
+// first_qt = the first query tile with more than one range.
+struct SplitPlan {
+  int tiles, units, first_qt;
+  size_t bytes;
+};
+hipError_t attn_split_plan(const AttnParams& p, int dtype, int d_qk, int d_v, SplitPlan* plan);
 
 // FP8 probability modes.  Lean: the e4m3 code of 2^x written from one FMA on
 // the log2-domain score; exact: exp2 and the hardware e4m3 conversion.  Both

@@ -46,11 +46,25 @@ int validate_attn_fwd(const void* q, const void* k, const void* v, void* out, co
   return MIATTN_OK;
 }
 
+miattn::AttnParams shape_params(int B, int Hq, int Hkv, int Nq, int Nk, int dtype, bool block64, int p_mode) {
+  miattn::AttnParams p{};
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.block64 = block64 ? 1 : 0;
+  p.p_mode = dtype == MIATTN_DTYPE_FP8_E4M3 ? p_mode : miattn::kPLean;  // BF16 has one mode
+  return p;
+}
+
+// ws == nullptr: no key split.  Otherwise the launch splits its keys when the
+// plan for the current device says so, with the workspace at ws.
 int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
                  int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
                  const float* v_scale, double tau, void* stream, bool block64 = false,
-                 int p_mode = MIATTN_P_DEFAULT) {
-  miattn::AttnParams p;
+                 int p_mode = MIATTN_P_DEFAULT, void* ws = nullptr, size_t ws_bytes = 0) {
+  miattn::AttnParams p = shape_params(B, Hq, Hkv, Nq, Nk, dtype, block64, p_mode);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -59,14 +73,18 @@ int run_attn_fwd(const void* q, const void* k, const void* v, void* out, float* 
   p.q_scale = q_scale;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.Nq = Nq;
-  p.Nk = Nk;
   p.sm_scale_log2 = (float)(1.4426950408889634 * tau);  // log2-domain softmax scale
-  p.block64 = block64 ? 1 : 0;
-  p.p_mode = dtype == MIATTN_DTYPE_FP8_E4M3 ? p_mode : miattn::kPLean;  // BF16 has one mode
+  if (ws != nullptr) {
+    miattn::SplitPlan plan;
+    if (miattn::attn_split_plan(p, dtype, d_qk, d_v, &plan) != hipSuccess) return MIATTN_ERR_HIP;
+    if (plan.tiles > 0) {
+      if (ws_bytes < plan.bytes) return MIATTN_ERR_SIZE;
+      p.split_tiles = plan.tiles;
+      p.split_units = plan.units;
+      p.ws_o = static_cast<float*>(ws);
+      p.ws_lse = p.ws_o + (size_t)B * Hq * plan.units * miattn::kQueryTile * d_v;
+    }
+  }
   const hipError_t e = miattn::launch_attn_fwd(p, dtype, d_qk, d_v, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
@@ -168,6 +186,51 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* 
   const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
   return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, MIATTN_DTYPE_FP8_E4M3, q_scale, k_scale,
                       v_scale, tau, stream, scales == MIATTN_SCALES_BLOCK64, p_mode);
+}
+
+int attn_fwd_ws_size(int B, int Hq, int Hkv, int Nq, int Nk, int d_qk, int d_v, int dtype, int scales, int p_mode,
+                     size_t* bytes) {
+  if (!bytes) return MIATTN_ERR_NULL;
+  *bytes = 0;
+  if (dtype != MIATTN_DTYPE_BF16 && dtype != MIATTN_DTYPE_FP8_E4M3) return MIATTN_ERR_DTYPE;
+  if (scales != MIATTN_SCALES_HEAD && scales != MIATTN_SCALES_BLOCK64) return MIATTN_ERR_DTYPE;
+  if (p_mode < MIATTN_P_LEAN || p_mode > MIATTN_P_EXACT_TILE) return MIATTN_ERR_DTYPE;
+  if (B < 0 || Nq < 0 || Nk < Nq || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return MIATTN_ERR_SIZE;
+  if (!supported_dims(d_qk, d_v)) return MIATTN_ERR_SHAPE;
+  if (B == 0 || Nq == 0) return MIATTN_OK;
+  const bool block64 = dtype == MIATTN_DTYPE_FP8_E4M3 && scales == MIATTN_SCALES_BLOCK64;
+  const miattn::AttnParams p = shape_params(B, Hq, Hkv, Nq, Nk, dtype, block64, p_mode);
+  miattn::SplitPlan plan;
+  if (miattn::attn_split_plan(p, dtype, d_qk, d_v, &plan) != hipSuccess) return MIATTN_ERR_HIP;
+  *bytes = plan.bytes;
+  return MIATTN_OK;
+}
+
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Nq,
+                int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                const float* v_scale, float softmax_scale, int scales, int p_mode, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (scales != MIATTN_SCALES_HEAD && scales != MIATTN_SCALES_BLOCK64) return MIATTN_ERR_DTYPE;
+  if (p_mode < MIATTN_P_LEAN || p_mode > MIATTN_P_EXACT_TILE) return MIATTN_ERR_DTYPE;
+  if (!(softmax_scale == 0.0f || (std::isfinite(softmax_scale) && softmax_scale > 0.0f))) return MIATTN_ERR_VALUE;
+  const int st =
+      validate_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, dtype, q_scale, k_scale, v_scale);
+  if (st != MIATTN_OK) return st;
+  const bool block64 = dtype == MIATTN_DTYPE_FP8_E4M3 && scales == MIATTN_SCALES_BLOCK64;
+  if (block64 && Nk > miattn::kBlock64MaxKeys) return MIATTN_ERR_SIZE;
+  if (B == 0 || Nq == 0) return MIATTN_OK;
+  size_t need = 0;
+  const int sst = attn_fwd_ws_size(B, Hq, Hkv, Nq, Nk, d_qk, d_v, dtype, scales, p_mode, &need);
+  if (sst != MIATTN_OK) return sst;
+  if (need > 0) {
+    if (!workspace) return MIATTN_ERR_NULL;
+    if (!aligned(workspace, 16)) return MIATTN_ERR_ALIGN;
+    if (workspace_bytes < need) return MIATTN_ERR_SIZE;
+  }
+  const double tau = softmax_scale == 0.0f ? 1.0 / std::sqrt((double)d_qk) : (double)softmax_scale;
+  return run_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d_qk, d_v, dtype, q_scale, k_scale, v_scale, tau,
+                      stream, block64, dtype == MIATTN_DTYPE_FP8_E4M3 ? p_mode : MIATTN_P_LEAN,
+                      need > 0 ? workspace : nullptr, workspace_bytes);
 }
 
 int attn_quantize_fp8_block64(const void* x, int x_dtype, void* x_fp8, float* scale, int B, int H, int N, int d,

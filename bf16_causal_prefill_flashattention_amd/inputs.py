@@ -78,6 +78,8 @@ WORKLOADS = {
     "bf16_gqa_n16k": _w("bf16_gqa_n16k", "bf16", 1, 32, 8, 16384, 128, 128, outliers=4,
                         note="GQA, activation-like outlier channels"),
     "fp8_mha_n1k": _w("fp8_mha_n1k", "fp8", 1, 32, 32, 1024, 128, 128),
+    "bf16_mha_n1k": _w("bf16_mha_n1k", "bf16", 1, 32, 32, 1024, 128, 128,
+                       note="BF16 point of the short-sequence case"),
     "fp8_mha_n4k": _w("fp8_mha_n4k", "fp8", 1, 32, 32, 4096, 128, 128),
     "fp8_mha_n16k": _w("fp8_mha_n16k", "fp8", 1, 32, 32, 16384, 128, 128),
     "fp8_mha_n32k": _w("fp8_mha_n32k", "fp8", 1, 32, 32, 32768, 128, 128),

@@ -17,11 +17,13 @@
 #ifndef MIATTN_H_
 #define MIATTN_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 5
+#define MIATTN_ABI_VERSION 6
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -64,9 +66,8 @@ extern "C" {
  *   q_scale [B, Hq], k_scale [B, Hkv], v_scale [B, Hkv]   (device memory)
  * The scales are folded into the scores before the softmax and into the
  * output; probabilities are rounded to e4m3 for the P.V product with lean P
- * against each 128-key tile's own maximum (MIATTN_P_DEFAULT, see
- * attn_fwd_fp8), so keys are lost only about 12 octaves below the maximum of
- * their own tile.
+ * against each key tile's own maximum (MIATTN_P_DEFAULT, see attn_fwd_fp8),
+ * so keys are lost only about 12 octaves below the maximum of their own tile.
  * dtype = MIATTN_DTYPE_BF16: the scale pointers are ignored and may be NULL.
  *
  * Sizes: B >= 0, N >= 0 (B == 0 or N == 0 is an empty call: success, nothing
@@ -224,9 +225,10 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
                                   max, in [0, 126]); the scaled MFMAs multiply them by 2^-k */
 #define MIATTN_P_EXACT 2       /* exp2 and the hardware round-to-nearest-even e4m3 conversion */
 #define MIATTN_P_EXACT_BLOCK 3 /* exact, with the per-64-key shift of MIATTN_P_LEAN_BLOCK */
-#define MIATTN_P_LEAN_TILE 4   /* lean P, and each query's probabilities of every 128-key tile
-                                  shifted up by 2^k (k = min(floor(running max - their max), 126));
-                                  the scaled MFMAs multiply them by 2^-k */
+#define MIATTN_P_LEAN_TILE 4   /* lean P, and each query's probabilities of every key tile (192
+                                  keys at d_qk = 128 with per-head scales, else 128) shifted up by
+                                  2^k (k = min(floor(running max - their max), 126)); the scaled
+                                  MFMAs multiply them by 2^-k */
 #define MIATTN_P_EXACT_TILE 5  /* exact, with the per-tile shift of MIATTN_P_LEAN_TILE */
 #define MIATTN_P_DEFAULT MIATTN_P_LEAN_TILE /* the mode of attn_fwd and attn_fwd_chunk on FP8 inputs */
 
@@ -250,7 +252,7 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
  * (2^-12 of it) is rounded to zero (below about 15 octaves) or to a subnormal
  * e4m3 value; rows whose softmax mass lies largely that far below their
  * largest score (long rows of keys whose magnitudes vary by block) lose that
- * mass.  The block and tile modes round every 64-key step or 128-key tile
+ * mass.  The block and tile modes round every 64-key step or key tile
  * against its own maximum, so only keys about 12 octaves below the maximum of
  * their own step or tile are lost.
  * scales or p_mode outside the values above: MIATTN_ERR_DTYPE.
@@ -258,6 +260,55 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d_qk, int d_v, const float* q_scale, const float* k_scale, const float* v_scale,
                  float softmax_scale, int scales, int p_mode, void* stream);
+
+/* Workspace of attn_fwd_ws: the bytes a launch with these arguments needs on
+ * the current device, written to *bytes; 0 when the launch does not split its
+ * keys (then attn_fwd_ws needs no workspace).
+ *
+ * Arguments as attn_fwd_ws (no tensors).  bytes NULL: MIATTN_ERR_NULL; invalid
+ * arguments give attn_fwd_ws's error codes, with *bytes = 0.  The figure
+ * depends on the device's compute-unit count, so query it with the device of
+ * the launch current.
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_ws_size(int B, int Hq, int Hkv, int Nq, int Nk, int d_qk, int d_v, int dtype, int scales, int p_mode,
+                     size_t* bytes);
+
+/* Causal attention with a caller-provided workspace, which lets short launches
+ * split their keys.
+ *
+ * Defines: the causal forward attention of attn_fwd_chunk (BF16, dtype =
+ * MIATTN_DTYPE_BF16: scales and p_mode are checked but not used) or
+ * attn_fwd_fp8 (dtype = MIATTN_DTYPE_FP8_E4M3) -- see there for the pages'
+ * passages -- evaluated with the online softmax over key ranges whose partial
+ * results are combined through their log-sum-exp, the identity that makes the
+ * tiled evaluation exact ([P1] "Why prefill attention deserves dedicated
+ * optimization": the scores are never materialised).
+ *
+ * Work split: the kernel gives each 256-query tile of a (batch, head) to one
+ * workgroup, so a launch with fewer query tiles than compute units (short
+ * sequences, or a short chunk against a long prefix) leaves units idle and
+ * takes as long as its last query tile, which walks every key.  When
+ * attn_fwd_ws_size is positive, every query tile is cut into ranges of at most
+ * L key tiles, L the smallest for which every range gets a compute unit of its
+ * own; the ranges of a query tile with more than one are written to the
+ * workspace (normalised fp32 rows and log2 sums of exp) and merged in a second
+ * kernel, in range order.
+ * Layout, sizes, scales, softmax_scale, lse, stream and asynchrony as
+ * attn_fwd_chunk / attn_fwd_fp8.  The result is bitwise reproducible from
+ * launch to launch on one device (no atomics, fixed merge order); it may
+ * differ in the last bits from attn_fwd_chunk / attn_fwd_fp8 where the launch
+ * splits.
+ * workspace: device memory of at least attn_fwd_ws_size bytes, 16-byte
+ * aligned, owned by the caller; the call's kernels use it as scratch, so no
+ * work that may run at the same time may use it; its contents afterwards are
+ * unspecified.  May be NULL when attn_fwd_ws_size is 0.  Too small:
+ * MIATTN_ERR_SIZE; NULL where it is needed: MIATTN_ERR_NULL; misaligned:
+ * MIATTN_ERR_ALIGN (nothing enqueued in each case).
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Nq,
+                int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                const float* v_scale, float softmax_scale, int scales, int p_mode, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -34,8 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_fwd_fp8", "attn_quantize_fp8",
-         "attn_quantize_fp8_block64", "attn_status_string", "attn_version"])
+        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_fwd_fp8", "attn_fwd_ws", "attn_fwd_ws_size",
+         "attn_quantize_fp8", "attn_quantize_fp8_block64", "attn_status_string", "attn_version"])
 
 
 def test_probability_mode_constants_match_the_binding():
@@ -166,6 +166,41 @@ def test_attn_fwd_fp8_validation(lib, kw, expect):
     assert fp8(lib, **kw) == expect
 
 
+def ws(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nk=20, dqk=128, dv=128, dtype=1, qs=P, ks=P, vs=P,
+       tau=0.0, scales=0, pmode=4, w=P, wb=1 << 20):
+    return lib.attn_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, dqk, dv, dtype, qs, ks, vs, tau, scales, pmode, w, wb,
+                           None)
+
+
+# (the workspace checks themselves need the device's compute-unit count: GPU tests)
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), E_NULL), (dict(o=None), E_NULL), (dict(qs=None), E_NULL), (dict(dtype=0, v=None), E_NULL),
+    (dict(Nq=21), E_SIZE), (dict(Hq=3, Hkv=2), E_SIZE), (dict(B=-1), E_SIZE),
+    (dict(Nq=8, Nk=(1 << 20) + 1, scales=1), E_SIZE),
+    (dict(dqk=64), E_SHAPE), (dict(dv=192), E_SHAPE),
+    (dict(lse=P + 2), E_ALIGN), (dict(k=P + 4), E_ALIGN),
+    (dict(tau=-1.0), E_VALUE), (dict(tau=float("nan")), E_VALUE),
+    (dict(scales=2), E_DTYPE), (dict(pmode=6), E_DTYPE), (dict(dtype=2), E_DTYPE), (dict(dtype=0, pmode=7), E_DTYPE),
+    (dict(Nq=0), OK), (dict(B=0), OK), (dict(Nq=0, w=None, wb=0), OK),
+    (dict(Nq=0, q=None, k=None, v=None, o=None, w=None), OK),
+])
+def test_attn_fwd_ws_validation(lib, kw, expect):
+    assert ws(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 2, 2, 8, 20, 128, 128, 2, 0, 4), E_DTYPE), ((1, 2, 2, 8, 20, 128, 128, 1, 2, 4), E_DTYPE),
+    ((1, 2, 2, 8, 20, 128, 128, 1, 0, 6), E_DTYPE), ((1, 3, 2, 8, 20, 128, 128, 1, 0, 4), E_SIZE),
+    ((1, 2, 2, 21, 20, 128, 128, 1, 0, 4), E_SIZE), ((1, 2, 2, 8, 20, 64, 128, 1, 0, 4), E_SHAPE),
+    ((0, 2, 2, 8, 20, 128, 128, 1, 0, 4), OK), ((1, 2, 2, 0, 20, 128, 128, 0, 0, 4), OK),
+])
+def test_attn_fwd_ws_size_validation(lib, args, expect):
+    n = ctypes.c_size_t(123)
+    assert lib.attn_fwd_ws_size(*args, ctypes.byref(n)) == expect
+    assert n.value == 0
+    assert lib.attn_fwd_ws_size(*args, None) == E_NULL
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 
@@ -190,6 +225,10 @@ def test_binding_refuses_cpu_tensors():
         pkg.attn_fwd_fp8(c, c, c, s, s, s, scales="tensor")
     with pytest.raises(ValueError):
         pkg.attn_fwd_fp8(c, c, c, s, s, s)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_ws(q, q, q)
+    with pytest.raises(ValueError):
+        pkg.attn_fwd_ws(c, c, c, s, s, s, p_mode="fast")
 
 
 def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
