@@ -117,6 +117,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float, ci,
                                 ci, vp, sz, vp]
     lib.attn_fwd_ws.restype = ci
+    lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, ci, ci, ci, ci, ci, ci, ci, ci, fp, fp, fp, ctypes.c_float,
+                                     ci, ci, vp]
+    lib.attn_fwd_noalloc.restype = ci
     lib.attn_status_string.argtypes = [ci]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmiattn.so")
 ATTN_FP8 = [f"attn_fwd_fp8_{s}_d{d}.hip" for s in ("head", "block64") for d in (128, 192)]
-SOURCES = ATTN_FP8 + ["attn_fwd_bf16.hip", "attn_fwd.hip", "quantize_fp8.hip", "miattn_api.cpp"]
+SOURCES = ATTN_FP8 + ["attn_fwd_bf16.hip", "attn_fwd.hip", "attn_fwd_noalloc.hip", "quantize_fp8.hip",
+                      "miattn_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

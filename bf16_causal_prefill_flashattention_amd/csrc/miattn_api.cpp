@@ -123,6 +123,7 @@ const char* attn_status_string(int status) {
     case MIATTN_ERR_HIP: return "the HIP runtime reported an error while enqueuing";
     case MIATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, scales and lse 4-byte alignment)";
     case MIATTN_ERR_VALUE: return "invalid scalar argument (softmax scale must be finite and positive, or 0)";
+    case MIATTN_ERR_SCRATCH: return "the launch needs more workspace than the static scratch of attn_fwd_noalloc holds";
     default: return "unknown status code";
   }
 }

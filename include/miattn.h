@@ -23,7 +23,7 @@
 extern "C" {
 #endif
 
-#define MIATTN_ABI_VERSION 6
+#define MIATTN_ABI_VERSION 7
 
 /* Element types of Q, K, V. */
 #define MIATTN_DTYPE_BF16 0     /* bfloat16 */
@@ -42,6 +42,7 @@ extern "C" {
 #define MIATTN_ERR_HIP (-5)      /* the HIP runtime reported an error when enqueuing */
 #define MIATTN_ERR_ALIGN (-6)    /* a tensor pointer is not 16-byte aligned (scales, lse: 4-byte) */
 #define MIATTN_ERR_VALUE (-7)    /* a scalar argument is out of range (softmax scale) */
+#define MIATTN_ERR_SCRATCH (-8)  /* attn_fwd_noalloc: the launch needs more than the static scratch holds */
 
 /* Causal forward attention, O = softmax(tau * Q K^T + causal mask) V.
  *
@@ -309,6 +310,31 @@ int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, float* l
                 int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
                 const float* v_scale, float softmax_scale, int scales, int p_mode, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Bytes of the static scratch attn_fwd_noalloc uses on each GPU: the most any
+ * key-split plan needs on a device with 256 compute units (256 ranges of 256
+ * fp32 rows of d_v = 128 plus their log2 sums of exp). */
+#define MIATTN_NOALLOC_SCRATCH_BYTES 33816576
+
+/* attn_fwd_ws without a workspace argument, allocating nothing.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The call is
+ * attn_fwd_ws (arguments, layout, results and errors as there) with its
+ * workspace in the library's own static scratch: a device array of
+ * MIATTN_NOALLOC_SCRATCH_BYTES bytes per GPU, part of the library's device
+ * code, held from the library's first use of that GPU until the process ends.
+ * The call allocates and frees nothing.  Every call on one GPU uses that GPU's
+ * one array, so calls that can overlap on one GPU (other streams, other host
+ * threads) race on it: the caller must order them (one stream, or events).
+ * Nothing in it needs to start at zero; its contents after a call are
+ * unspecified.  A launch whose split plan needs more than the array holds
+ * (possible only on devices with more than 256 compute units):
+ * MIATTN_ERR_SCRATCH, nothing enqueued.
+ * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                     int Nq, int Nk, int d_qk, int d_v, int dtype, const float* q_scale, const float* k_scale,
+                     const float* v_scale, float softmax_scale, int scales, int p_mode, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

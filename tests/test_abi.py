@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert sorted(declared_functions()) == sorted(
-        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_fwd_fp8", "attn_fwd_ws", "attn_fwd_ws_size",
+        ["attn_fwd", "attn_fwd_chunk", "attn_fwd_block64", "attn_fwd_fp8", "attn_fwd_noalloc", "attn_fwd_ws",
+         "attn_fwd_ws_size",
          "attn_quantize_fp8", "attn_quantize_fp8_block64", "attn_status_string", "attn_version"])
 
 
@@ -56,7 +57,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert pkg.attn_version() == header_constant("MIATTN_ABI_VERSION")
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = pkg.attn_status_string(code)
         assert s and s != "unknown status code"
     assert pkg.attn_status_string(-99) == "unknown status code"

@@ -26,7 +26,7 @@ import pytest
 from bf16_causal_prefill_flashattention_amd import build as B
 
 pytestmark = pytest.mark.cpu
-ATTN_SOURCES = [s for s in B.SOURCES if s.startswith("attn_fwd_") and s.endswith(".hip")]
+ATTN_SOURCES = B.ATTN_FP8 + ["attn_fwd_bf16.hip"]  # the translation units that instantiate the kernel
 VALU_SGPR_STATES = 5
 M0_STATES = 1
 
