@@ -385,6 +385,48 @@ def roofline(w, attn_ms, flops=None, clock=None):
     }
 
 
+# (instruction form, byte stride between lanes, expected bank behaviour) of the probe kernels
+LDS_PROBES = [
+    (0, 4, "ds_read_b32, consecutive words: conflict-free"),
+    (0, 8, "ds_read_b32, every other word: 2-way conflict"),
+    (0, 256, "ds_read_b32, all lanes in bank 0"),
+    (1, 16, "ds_read_b128, consecutive 16-byte chunks: conflict-free"),
+    (1, 256, "ds_read_b128, every chunk starting at bank 0"),
+    (2, 8, "ds_read_b64_tr_b8, consecutive 8-byte pieces"),
+    (2, 256, "ds_read_b64_tr_b8, every piece at bank 0"),
+]
+
+
+def lds_probe(blocks: int = 256, iters: int = 4096):
+    """Run every LDS probe kernel once (one workgroup per CU); one JSON line."""
+    import ctypes
+
+    import torch
+
+    from bf16_causal_prefill_flashattention_amd import build as B
+
+    if not torch.cuda.is_available():
+        print("bench.py --lds-probe needs a GPU", file=sys.stderr)
+        return 1
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.lds_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.lds_probe_run.restype = ctypes.c_int
+    out = torch.zeros(blocks * lib.lds_probe_threads(), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    runs = []
+    for kind, stride, what in LDS_PROBES:
+        st = lib.lds_probe_run(kind, stride, blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        if st != 0:
+            print(f"lds_probe_run({kind}, {stride}) failed: {st}", file=sys.stderr)
+            return 1
+        runs.append({"kernel": f"lds_probe_kernel<{kind}, {stride}>", "pattern": what,
+                     "lds_instructions": blocks * (lib.lds_probe_threads() // 64) * iters})
+    print(json.dumps({"lds_probe": runs, "blocks": blocks, "iters_per_wave": iters}), flush=True)
+    return 0
+
+
 def clock_study(seconds: float):
     """One JSON line per (dtype, input distribution): the data-dependent clock
     and energy of the attention kernel on the 32K workloads."""
@@ -514,6 +556,9 @@ def main(argv=None):
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-block64", action="store_true")
     ap.add_argument("--clock-study", action="store_true")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="run the LDS read patterns of known bank behaviour (libmiattn_probe.so) once each, "
+                         "for reading the LDS bank-conflict counter against them under rocprofv3 --pmc")
     ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -526,6 +571,8 @@ def main(argv=None):
         return 2
     if args.clock_study:
         return clock_study(args.study_seconds)
+    if args.lds_probe:
+        return lds_probe()
 
     from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS
 

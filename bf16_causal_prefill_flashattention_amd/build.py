@@ -16,9 +16,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmiattn.so")
+PROBE_LIB = os.path.join(PKG, "libmiattn_probe.so")
 ATTN_FP8 = [f"attn_fwd_fp8_{s}_d{d}.hip" for s in ("head", "block64") for d in (128, 192)]
 SOURCES = ATTN_FP8 + ["attn_fwd_bf16.hip", "attn_fwd.hip", "attn_fwd_noalloc.hip", "quantize_fp8.hip",
                       "miattn_api.cpp"]
+# measurement aid of bench.py --lds-probe (LDS reads of known bank behaviour), its own library
+PROBE_SOURCES = ["lds_probe.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -64,22 +67,29 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print("\n".join(msgs), flush=True)
 
 
+def _link(objs, lib: str, tmp: str, verbose: bool) -> None:
+    out_tmp = os.path.join(tmp, os.path.basename(lib))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    shutil.copyfile(out_tmp, lib + ".tmp")
+    os.replace(lib + ".tmp", lib)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmiattn.so next to this file.
-    Always recompiles.  Returns the library path."""
+    """Compile every source for gfx950 and link libmiattn.so (and the LDS
+    counter probe, libmiattn_probe.so) next to this file.  Always recompiles.
+    Returns the path of libmiattn.so."""
     with tempfile.TemporaryDirectory(prefix="miattn_build_") as tmp:
-        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-        out_tmp = os.path.join(tmp, "libmiattn.so")
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"linking libmiattn.so failed:\n{r.stdout}\n{r.stderr}")
-        shutil.copyfile(out_tmp, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
+        srcs = SOURCES + PROBE_SOURCES
+        objs = [os.path.join(tmp, s + ".o") for s in srcs]
+        with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+            list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+        _link(objs[:len(SOURCES)], LIB, tmp, verbose)
+        _link(objs[len(SOURCES):], PROBE_LIB, tmp, verbose)
     return LIB
 
 

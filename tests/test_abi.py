@@ -250,3 +250,15 @@ def test_flash_attn_func_refuses_what_the_kernels_do_not_compute():
         pkg.flash_attn_func(q, q, q, fp8=True, p_block_scale=True)
     with pytest.raises(ValueError):  # CPU tensors
         pkg.flash_attn_func(q, q, q)
+
+
+def test_probe_library_exports_its_entry_points():
+    """The LDS counter probe (bench.py --lds-probe) is built beside the library."""
+    from bf16_causal_prefill_flashattention_amd import build as B
+
+    out = subprocess.run(["nm", "-D", "--defined-only", B.PROBE_LIB], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {"lds_probe_run", "lds_probe_threads"} <= exported
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    assert lib.lds_probe_threads() == 256
+    assert lib.lds_probe_run(0, 4, 0, 16, None, None) == -1  # rejected before any launch
