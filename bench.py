@@ -427,29 +427,157 @@ def lds_probe(blocks: int = 256, iters: int = 4096):
     return 0
 
 
-def clock_study(seconds: float):
-    """One JSON line per (dtype, input distribution): the data-dependent clock
-    and energy of the attention kernel on the 32K workloads."""
-    import threading
-
-    import torch
-
-    import bf16_causal_prefill_flashattention_amd as miattn
-    from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS, make_qkv
-
+def amdsmi_gpu0():
+    """(amdsmi module, handle of the first GPU), or (None, None) when unavailable."""
     try:
         import amdsmi
 
         amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        return amdsmi, amdsmi.amdsmi_get_processor_handles()[0]
     except Exception as e:  # the readings are optional; timing still runs
         print(f"amdsmi unavailable ({e}); clock and power are not reported", file=sys.stderr)
-        handle = None
+        return None, None
+
+
+def sustained(launch, seconds: float, smi, flops: float):
+    """Back-to-back launches for about `seconds` (after 20 untimed ones), timed
+    with one event pair, with the GFX clock and the board energy counter
+    sampled every 50 ms.  Returns a dict: launches, ms per launch, TFLOP/s
+    (flops per launch), and with amdsmi the mean clock of the second half of
+    the samples, board watts and TFLOP/J."""
+    import threading
+
+    import torch
+
+    amdsmi, handle = smi
 
     def energy_j():
         r = amdsmi.amdsmi_get_energy_count(handle)
         return r["energy_accumulator"] * r["counter_resolution"] * 1e-6
 
+    for _ in range(20):
+        launch()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch()
+    e1.record()
+    torch.cuda.synchronize()
+    n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
+    clocks, energy, stop = [], [], threading.Event()
+
+    def sample():
+        while not stop.wait(0.05):
+            try:
+                clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+                energy.append((time.perf_counter(), energy_j()))
+            except Exception:
+                pass
+
+    th = None
+    if handle is not None:
+        th = threading.Thread(target=sample, daemon=True)
+        ej0, t0 = energy_j(), time.perf_counter()
+        th.start()
+    e0.record()
+    for _ in range(n):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    rec = {"launches": n, "ms_per_launch": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    if th is not None:
+        t1, ej1 = time.perf_counter(), energy_j()
+        stop.set()
+        th.join()
+        # The energy counter advances in coarse steps (about once a second on
+        # MI355X boards): the rate between its first and last change inside
+        # the window is the board power; the clock reading lags the load, so
+        # only its second half is kept.
+        watts = (ej1 - ej0) / (t1 - t0)
+        steps = [energy[i] for i in range(1, len(energy)) if energy[i][1] != energy[i - 1][1]]
+        rec["energy_steps"] = len(steps)
+        if len(steps) >= 2 and steps[-1][0] > steps[0][0]:
+            watts = (steps[-1][1] - steps[0][1]) / (steps[-1][0] - steps[0][0])
+        clocks = clocks[len(clocks) // 2:]
+        rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
+        rec["sclk_samples"] = len(clocks)
+        rec["board_watts_mean"] = round(watts, 1)
+        rec["tflop_per_joule"] = round(rec["tflops"] / watts, 3) if watts > 0 else None
+    return rec
+
+
+def mfma_probe(seconds: float):
+    """Back-to-back MFMAs on operands with the attention inputs' values (Gaussian
+    BF16; e4m3 codes of Gaussian data at a per-head scale; or, as in a P.V
+    product, probabilities in [0, 1) against Gaussian values), sustained for
+    about `seconds`: the matrix-core throughput, clock and board power the
+    power limit allows on such data, the ceiling of an attention kernel on it.
+    One JSON line per (dtype, operands)."""
+    import ctypes
+
+    import torch
+
+    from bf16_causal_prefill_flashattention_amd import build as B
+
+    if not torch.cuda.is_available():
+        print("bench.py --mfma-probe needs a GPU", file=sys.stderr)
+        return 1
+    smi = amdsmi_gpu0()
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.mfma_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count  # one workgroup (8 waves) per CU
+    threads = lib.mfma_probe_threads()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    for fp8, iters in ((False, 16384), (True, 8192)):
+        words = lib.mfma_probe_words(1 if fp8 else 0)  # A sets, then B sets, per thread
+        per = words // 2 * (4 if fp8 else 2)  # values of A (and of B) per thread
+        for label in ("gaussian", "probabilities_x_gaussian"):
+            b_vals = torch.randn(blocks * threads, per, generator=g)
+            if label == "gaussian":
+                a_vals = torch.randn(blocks * threads, per, generator=g)
+            else:  # A in [0, 1): a P.V product's probabilities (x 2^6 before e4m3 rounding in the FP8 kernel)
+                a_vals = torch.rand(blocks * threads, per, generator=g) * (64.0 if fp8 else 1.0)
+            if fp8:  # e4m3 codes at a per-head scale of Gaussian data (amax about 4.5 sigma -> 448)
+                if label == "gaussian":
+                    a_vals = a_vals * (448.0 / 4.5)
+                b_vals = b_vals * (448.0 / 4.5)
+                enc = lambda t: t.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)  # noqa: E731
+            else:
+                enc = lambda t: t.to(torch.bfloat16)  # noqa: E731
+            ops = torch.cat([enc(a_vals), enc(b_vals)], dim=1).contiguous().view(torch.int32).reshape(-1).to(dev)
+            assert ops.numel() == blocks * threads * words
+            out = torch.empty(blocks * threads, dtype=torch.float32, device=dev)
+            stream = torch.cuda.current_stream().cuda_stream
+
+            def launch():
+                st = lib.mfma_probe_run(1 if fp8 else 0, blocks, iters, ctypes.c_void_p(ops.data_ptr()),
+                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+                if st != 0:
+                    raise RuntimeError(f"mfma_probe_run failed: {st}")
+
+            flops = blocks * (threads // 64) * 4 * iters * (32 * 32 * (64 if fp8 else 16) * 2)
+            rec = {"study": "mfma_probe", "dtype": "fp8_e4m3" if fp8 else "bf16", "operands": label,
+                   "mfma": "32x32x64 f8f6f4" if fp8 else "32x32x16 bf16", "peak_tflops": PEAK_TFLOPS["fp8" if fp8 else "bf16"]}
+            rec.update(sustained(launch, seconds, smi, flops))
+            rec["frac_of_peak"] = round(rec["tflops"] / rec["peak_tflops"], 4)
+            print(json.dumps(rec), flush=True)
+    return 0
+
+
+def clock_study(seconds: float):
+    """One JSON line per (dtype, input distribution): the data-dependent clock
+    and energy of the attention kernel on the 32K workloads."""
+    import torch
+
+    import bf16_causal_prefill_flashattention_amd as miattn
+    from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS, make_qkv
+
+    handle = amdsmi_gpu0()
     dev = torch.device("cuda:0")
     cases = [
         ("gaussian", lambda q, k, v: (q, k, v)),
@@ -482,58 +610,8 @@ def clock_study(seconds: float):
                 else:
                     launch = (lambda m: lambda: miattn.attn_fwd_fp8(cq, ck, cv, sq, sk, sv, out=out,  # noqa: E731
                                                                       with_lse=False, p_mode=m))(mode)
-                for _ in range(20):
-                    launch()
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                launch()
-                e1.record()
-                torch.cuda.synchronize()
-                n = max(10, int(seconds * 1e3 / e0.elapsed_time(e1)))
-                clocks, energy, stop = [], [], threading.Event()
-
-                def sample():
-                    while not stop.wait(0.05):
-                        try:
-                            clocks.append(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-                            energy.append((time.perf_counter(), energy_j()))
-                        except Exception:
-                            pass
-
-                th = None
-                if handle is not None:
-                    th = threading.Thread(target=sample, daemon=True)
-                    ej0, t0 = energy_j(), time.perf_counter()
-                    th.start()
-                e0.record()
-                for _ in range(n):
-                    launch()
-                e1.record()
-                torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / n
-                rec = {"study": "clock_energy", "workload": wname, "inputs": cname, "p_mode": mode or "bf16",
-                       "launches": n, "ms_per_launch": round(ms, 4),
-                       "tflops": round(w.causal_flops / (ms * 1e-3) / 1e12, 1)}
-                if th is not None:
-                    t1, ej1 = time.perf_counter(), energy_j()
-                    stop.set()
-                    th.join()
-                    # The energy counter advances in coarse steps (about once a second on
-                    # MI355X boards): the rate between its first and last change inside
-                    # the window is the board power; the clock reading lags the load, so
-                    # only its second half is kept.
-                    watts = (ej1 - ej0) / (t1 - t0)
-                    steps = [energy[i] for i in range(1, len(energy)) if energy[i][1] != energy[i - 1][1]]
-                    rec["energy_steps"] = len(steps)
-                    if len(steps) >= 2 and steps[-1][0] > steps[0][0]:
-                        watts = (steps[-1][1] - steps[0][1]) / (steps[-1][0] - steps[0][0])
-                    clocks = clocks[len(clocks) // 2:]
-                    rec["sclk_mhz_mean"] = round(sum(clocks) / len(clocks), 1) if clocks else None
-                    rec["sclk_samples"] = len(clocks)
-                    rec["board_watts_mean"] = round(watts, 1)
-                    rec["tflop_per_joule"] = round(rec["tflops"] / watts, 3) if watts > 0 else None
+                rec = {"study": "clock_energy", "workload": wname, "inputs": cname, "p_mode": mode or "bf16"}
+                rec.update(sustained(launch, seconds, handle, w.causal_flops))
                 print(json.dumps(rec), flush=True)
             del out, q, k, v
             if w.dtype == "fp8":
@@ -556,6 +634,9 @@ def main(argv=None):
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-block64", action="store_true")
     ap.add_argument("--clock-study", action="store_true")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="sustain back-to-back MFMAs on attention-like operands (libmiattn_probe.so) for "
+                         "--study-seconds: the throughput the board power limit allows on such data")
     ap.add_argument("--lds-probe", action="store_true",
                     help="run the LDS read patterns of known bank behaviour (libmiattn_probe.so) once each, "
                          "for reading the LDS bank-conflict counter against them under rocprofv3 --pmc")
@@ -573,6 +654,8 @@ def main(argv=None):
         return clock_study(args.study_seconds)
     if args.lds_probe:
         return lds_probe()
+    if args.mfma_probe:
+        return mfma_probe(args.study_seconds)
 
     from bf16_causal_prefill_flashattention_amd.inputs import WORKLOADS
 

@@ -20,8 +20,9 @@ PROBE_LIB = os.path.join(PKG, "libmiattn_probe.so")
 ATTN_FP8 = [f"attn_fwd_fp8_{s}_d{d}.hip" for s in ("head", "block64") for d in (128, 192)]
 SOURCES = ATTN_FP8 + ["attn_fwd_bf16.hip", "attn_fwd.hip", "attn_fwd_noalloc.hip", "quantize_fp8.hip",
                       "miattn_api.cpp"]
-# measurement aid of bench.py --lds-probe (LDS reads of known bank behaviour), its own library
-PROBE_SOURCES = ["lds_probe.hip"]
+# measurement aids of bench.py --lds-probe and --mfma-probe (LDS reads of known bank behaviour,
+# back-to-back MFMAs), in a library of their own
+PROBE_SOURCES = ["lds_probe.hip", "mfma_probe.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
