@@ -22,9 +22,14 @@
 // results of separate key ranges needs.
 //
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
-// (batch, query head); each wave owns 32 queries.  Key tiles hold 128 keys
-// (FP8), 96 (BF16, d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips the tiles
-// wholly above its queries and masks only the tiles that cross its diagonal.
+// (batch, query head); each wave owns 32 queries.  Key tiles hold 192 keys (FP8
+// at d_qk = 128 with per-head scales and no per-64-key shift), 128 (the other
+// FP8 variants), 96 (BF16, d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips
+// the tiles wholly above its queries and masks only the tiles that cross its
+// diagonal.  A split launch gives each workgroup one range of a query tile's
+// key tiles instead (the kernel's SPLIT instantiation): ranges of a query tile
+// with more than one write normalised fp32 rows and their log2 sum of exp, and
+// a merge kernel combines them.
 //
 // Matrix layout.  A wave computes S^T = K_tile * Q^T (keys on MFMA rows,
 // queries on MFMA columns), so lane l owns query (l % 32) and holds half of the
@@ -74,7 +79,7 @@
 // probabilities by a fixed 2^6 first.  Lean codes reach about 13 octaves below
 // that (the exact conversion's subnormals about 2.5 further), so key blocks
 // whose scores lie far below the running max would round to zero; a shift
-// keeps them: each query's probabilities of a 128-key tile (tile mode, the
+// keeps them: each query's probabilities of a key tile (tile mode, the
 // default) or of a 64-key P.V step (block mode, the pages' per-64-key
 // power-of-two scaling of P undone by the scaled MFMA) are shifted up by k
 // octaves, k = floor(running max - their max), and the P.V MFMA scales them
