@@ -90,6 +90,42 @@ def test_weights_rows_sum_to_one_and_causal_zeros():
         assert np.all(w >= 0)
 
 
+def test_weights_of_two_keys_are_a_logistic_of_the_scaled_score_gap():
+    """Closed form that fixes tau: row 1 sees keys 0 and 1, so its weight on key
+    1 is 1 / (1 + exp(-tau (s1 - s0))), s_j = <q_1, k_j>; checked at the default
+    tau = 1/sqrt(d) and at explicit scales."""
+    rng = np.random.default_rng(40)
+    d = 64
+    q = rng.standard_normal((1, 2, 1, d))
+    k = rng.standard_normal((1, 2, 1, d))
+    gap = float(q[0, 1, 0] @ k[0, 1, 0] - q[0, 1, 0] @ k[0, 0, 0])
+    for tau in (None, 0.05, 0.3, 1.0):
+        t = 1.0 / math.sqrt(d) if tau is None else tau
+        w = causal_weights_ref(q, k, softmax_scale=tau)
+        assert w[0, 0] == 1.0 and w[0, 1] == 0.0
+        assert abs(w[1, 1] - 1.0 / (1.0 + math.exp(-t * gap))) <= 1e-15
+        assert abs(w[1, 0] - 1.0 / (1.0 + math.exp(t * gap))) <= 1e-15
+
+
+def test_zero_queries_give_uniform_weights_and_weights_reproduce_the_output():
+    """Q = 0: W[i, j] = 1 / (i + 1) for j <= i (any tau).  Random inputs with
+    GQA: W @ V of each head equals attn_ref's output, which the SDPA and
+    brute-force pins fix."""
+    N = 40
+    q0 = np.zeros((1, N, 2, 32))
+    k = _rand((1, N, 1, 32), 41)
+    w = causal_weights_ref(q0, k, 0, 1, softmax_scale=0.7)
+    expect = np.tril(np.ones((N, N))) / np.arange(1, N + 1)[:, None]
+    np.testing.assert_allclose(w, expect, rtol=0, atol=1e-15)
+    q = _rand((1, N, 4, 32), 42)
+    k = _rand((1, N, 2, 32), 43)
+    v = _rand((1, N, 2, 16), 44)
+    out = attn_ref(q, k, v)
+    for h in range(4):
+        w = causal_weights_ref(q, k, 0, h)
+        np.testing.assert_allclose(w @ v[0, :, h // 2, :], out[0, :, h, :], rtol=1e-12, atol=1e-13)
+
+
 def test_row_zero_is_first_value_row_exactly():
     q = _rand((2, 50, 4, 128), 30)
     k = _rand((2, 50, 2, 128), 31)

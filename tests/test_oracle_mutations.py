@@ -127,3 +127,39 @@ def test_block64_mutants_are_caught(old, new):
             amax = np.abs(ref[0, 64 * j:64 * (j + 1)]).max()
             ok &= bool(224 < amax / float(scales[0, 0, j]) <= 448 * (1 + 1e-6))
     assert not ok
+
+
+WEIGHT_MUTANTS = [
+    ("s = tau * (q[b, :, h, :] @ k[b, :, g, :].T)", "s = (q[b, :, h, :] @ k[b, :, g, :].T)"),  # tau dropped
+    ("s = tau * (q[b, :, h, :] @ k[b, :, g, :].T)", "s = tau * tau * (q[b, :, h, :] @ k[b, :, g, :].T)"),  # tau twice
+    ("np.tril(np.ones((N, N), dtype=bool))", "np.tril(np.ones((N, N), dtype=bool), 1)"),  # one key past the diagonal
+    ("g = h // (Hq // Hkv)\n    N = q.shape[1]", "g = h % Hkv\n    N = q.shape[1]"),  # interleaved GQA mapping
+]
+
+
+def _weights_ok(weights):
+    """The two-key logistic closed form and W @ V = attn_ref (the pins of the
+    weight matrix in test_oracle_attention.py)."""
+    from oracle import attn_ref
+
+    g = np.random.default_rng(7)
+    q, k = g.standard_normal((1, 2, 1, 64)), g.standard_normal((1, 2, 1, 64))
+    gap = float(q[0, 1, 0] @ k[0, 1, 0] - q[0, 1, 0] @ k[0, 0, 0])
+    ok = abs(weights(q, k)[1, 1] - 1.0 / (1.0 + math.exp(-gap / 8.0))) <= 1e-15
+    q, k, v = g.standard_normal((1, 30, 4, 32)), g.standard_normal((1, 30, 2, 32)), g.standard_normal((1, 30, 2, 8))
+    out = attn_ref(q, k, v)
+    for h in range(4):
+        w = weights(q, k, 0, h)
+        ok &= bool(np.allclose(w @ v[0, :, h // 2, :], out[0, :, h, :], rtol=1e-12, atol=1e-13))
+    return ok
+
+
+@pytest.mark.parametrize("old,new", WEIGHT_MUTANTS)
+def test_weight_mutants_are_caught(old, new):
+    m = _load_mutant("attention.py", old, new)
+    assert not _weights_ok(m.causal_weights_ref)
+
+
+def test_unmutated_weights_pass():
+    m = _load_mutant("attention.py", "import math", "import math")
+    assert _weights_ok(m.causal_weights_ref)
