@@ -361,20 +361,42 @@ enum PShift { kShiftNone = 0, kShiftStep = 1, kShiftTile = 2 };
 constexpr float kLeanC0 = 55.66f;
 constexpr float kLeanMagic = 12582912.0f;  // 1.5 * 2^23
 
-// Codes of four scores into one word, first score in the low byte.
-__device__ __forceinline__ uint32_t lean_p4(float s0, float s1, float s2, float s3, float c8, float b8, float magic) {
-  const float t0 = __builtin_fmaf(s0, c8, b8), t1 = __builtin_fmaf(s1, c8, b8);
-  const float t2 = __builtin_fmaf(s2, c8, b8), t3 = __builtin_fmaf(s3, c8, b8);
-  uint32_t w;
-  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
-      : "=v"(w) : "v"(t0), "v"(magic));
-  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
-      : "+v"(w) : "v"(t1), "v"(magic));
-  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
-      : "+v"(w) : "v"(t2), "v"(magic));
-  asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
-      : "+v"(w) : "v"(t3), "v"(magic));
-  return w;
+// Lean-P byte inserts of NBLK score blocks (their FMAs already applied):
+// byte j of word 4 blk + i is the code of score 4 i + j of block blk.
+template <int NBLK>
+__device__ __forceinline__ void lean_insert_bytes(uint32_t* pk, const f32x16 (&t)[NBLK], float magic) {
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = t[blk][4 * i];
+      asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+          : "=v"(pk[4 * blk + i]) : "v"(x), "v"(magic));
+    }
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = t[blk][4 * i + 1];
+      asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+          : "+v"(pk[4 * blk + i]) : "v"(x), "v"(magic));
+    }
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = t[blk][4 * i + 2];
+      asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+          : "+v"(pk[4 * blk + i]) : "v"(x), "v"(magic));
+    }
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = t[blk][4 * i + 3];
+      asm("v_max_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+          : "+v"(pk[4 * blk + i]) : "v"(x), "v"(magic));
+    }
 }
 
 template <class C, bool FP8, int DQK, int DV>
@@ -842,12 +864,15 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
         float bks[NBLK / 2];  // code offset of k-step ks
 #pragma unroll
         for (int ks = 0; ks < NBLK / 2; ++ks) bks[ks] = PSH != kShiftNone ? __builtin_fmaf(8.f, kst[ks], b8) : b8;
+        // Two passes: the FMAs in place, then the byte inserts byte-major over
+        // all words, so consecutive inserts are independent (the four inserts
+        // of one word form a chain: each keeps the bytes written before it).
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            wv.pk[4 * blk + i] = lean_p4(wv.s[blk][4 * i], wv.s[blk][4 * i + 1], wv.s[blk][4 * i + 2],
-                                         wv.s[blk][4 * i + 3], c8, bks[blk >> 1], magic);
+          for (int r = 0; r < 16; ++r) wv.s[blk][r] = __builtin_fmaf(wv.s[blk][r], c8, bks[blk >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        lean_insert_bytes<NBLK>(wv.pk, wv.s, magic);
       } else {
         // exact P: exp2 and the hardware round-to-nearest-even e4m3 conversion
         float bexp[NBLK / 2];  // log2-domain offset of k-step ks
