@@ -1017,23 +1017,48 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     return;
   }
   const float inv = sv / lsum;
-  if (my_q < Nq) {
-    // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
-    // log2 sum_j 2^x_j = m - SHIFT + log2(l); lanes l and l + 32 share a query
-    if (p.lse != nullptr && hl == 0)
-      p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(lsum)) * 0.69314718055994531f;
-    __bf16* O = static_cast<__bf16*>(p.out) + (((size_t)b * Nq + my_q) * p.Hq + h) * DV;
+  // the probabilities are 2^(x - m + SHIFT) for log2-domain scores x, so
+  // log2 sum_j 2^x_j = m - SHIFT + log2(l); lanes l and l + 32 share a query
+  if (p.lse != nullptr && hl == 0 && my_q < Nq)
+    p.lse[((size_t)b * p.Hq + h) * Nq + my_q] = (wv.st.m - C::SHIFT + __log2f(lsum)) * 0.69314718055994531f;
+  // The output rows go out through LDS.  In registers lane (query l32, half hl)
+  // holds 4-channel pieces of its row, so stores straight from them cover 16
+  // bytes of each of 32 rows per instruction; staged, every store writes four
+  // whole 256-byte rows.  Each wave stages its 32 rows (8 KB) in a region of
+  // its own, 16-byte chunk c of row r at chunk position c ^ (r & 15) (the
+  // writes of a lane half and the reads of a row then spread over all banks).
+  // Every tile load of the item has completed and every wave has left the
+  // loop, so the tile buffers are free; the barrier at the end keeps the next
+  // item's first loads and zero fill out of regions still being read.
+  static_assert(DV == 128, "the staging layout holds 256-byte rows");
+  static_assert(C::LDS_BYTES >= kWaves * 32 * DV * 2, "every wave's rows fit in the tile buffers");
+  uint8_t* const stage = smem + w * (32 * DV * 2);
+  // (the lane index passes through an empty asm so that the addresses below
+  // are computed here, per item, and not hoisted out of the item loop into
+  // registers that would be spilled across it)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int r32 = ln & 31;
 #pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
+  for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ch = d * 32 + 8 * i + 4 * hl;
-        const i32x2 v2 = {(int)pack_bf16x2(wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv),
-                          (int)pack_bf16x2(wv.st.o[d][4 * i + 2] * inv, wv.st.o[d][4 * i + 3] * inv)};
-        *reinterpret_cast<i32x2*>(O + ch) = v2;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = 4 * d + i;  // channels 8 chunk .. 8 chunk + 7; this lane's half at byte 8 hl
+      const i32x2 v2 = {(int)pack_bf16x2(wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv),
+                        (int)pack_bf16x2(wv.st.o[d][4 * i + 2] * inv, wv.st.o[d][4 * i + 3] * inv)};
+      *reinterpret_cast<i32x2*>(stage + r32 * (DV * 2) + 16 * (chunk ^ (r32 & 15)) + 8 * (ln >> 5)) = v2;
+    }
+  {
+    const int cc = ln & 15;  // the chunk this lane stores
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 4 * r + (ln >> 4), q = qw0 + row;
+      const i32x4 v4 = *reinterpret_cast<const i32x4*>(stage + row * (DV * 2) + 16 * (cc ^ (row & 15)));
+      if (q < Nq)
+        *reinterpret_cast<i32x4*>(static_cast<__bf16*>(p.out) + (((size_t)b * Nq + q) * p.Hq + h) * DV + 8 * cc) = v4;
     }
   }
+  barrier(false);
 }
 
 // Persistent workgroups (at most one per CU) walk a static list of work units.
