@@ -229,12 +229,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 // buffer load must not follow an SALU write of M0 directly (one wait state,
 // the s_nop 0 here), and must not read an SGPR written by a VALU instruction
 // (v_readfirstlane) within five wait states -- rsrc_words ends with those.
-__device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, const uint8_t* lds_block) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_block);
+__device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, uint32_t lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "{m0}"(lds)
                : "memory");
+}
+// The destination as a generic pointer into the LDS: converted (and
+// null-checked, on its 64 bits) at every load.  The key-split kernel uses the
+// 32-bit form above: with the pointers, the compiler keeps their high words and
+// spills them inside its main loop (each reload then waits for every tile load
+// in flight).  The unsplit kernels keep this form, with which their main loops
+// compile without spills (with the 32-bit form they gain some).
+__device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, const uint8_t* lds_block) {
+  load_to_lds(rsrc, voffset, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_block));
 }
 
 // Buffer resource words for raw 16-byte loads over [base, base + bytes): 32-bit
@@ -440,6 +448,17 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   static_assert(C::V_TILE % (16 * kThreads) == 0, "the zero-filled V buffer splits into whole stores");
   uint8_t* const Vs = smem;                 // V buffers 0, 1
   uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
+  // the tile loads' destinations (LDS byte addresses in the key-split kernel,
+  // generic pointers otherwise; see load_to_lds)
+  const uint32_t vs_lds = __builtin_amdgcn_readfirstlane(lds_addr(Vs));
+  auto k_dst = [&](int buf, int blk) __attribute__((always_inline)) {
+    if constexpr (SPLIT) return vs_lds + 2 * C::V_TILE + buf * C::K_TILE + 1024 * blk;
+    else return Ks + buf * C::K_TILE + 1024 * blk;
+  };
+  auto v_dst = [&](int buf, int blk) __attribute__((always_inline)) {
+    if constexpr (SPLIT) return vs_lds + buf * C::V_TILE + 1024 * blk;
+    else return Vs + buf * C::V_TILE + 1024 * blk;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -558,9 +577,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     for (int i = 0; i < C::K_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
       if constexpr (C::K_UNI)
-        load_to_lds(i == 0 ? rk : rsrc_advance(rk, i * k_blk_bytes), wv.k_dma[0], Ks + buf * C::K_TILE + 1024 * blk);
+        load_to_lds(i == 0 ? rk : rsrc_advance(rk, i * k_blk_bytes), wv.k_dma[0], k_dst(buf, blk));
       else
-        load_to_lds(rk, wv.k_dma[i], Ks + buf * C::K_TILE + 1024 * blk);
+        load_to_lds(rk, wv.k_dma[i], k_dst(buf, blk));
     }
   };
   auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
@@ -570,9 +589,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     for (int i = 0; i < C::V_PER_WAVE; ++i) {
       const int blk = w + kWaves * i;
       if constexpr (C::V_UNI)
-        load_to_lds(i == 0 ? rv : rsrc_advance(rv, i * v_blk_bytes), wv.v_dma[0], Vs + buf * C::V_TILE + 1024 * blk);
+        load_to_lds(i == 0 ? rv : rsrc_advance(rv, i * v_blk_bytes), wv.v_dma[0], v_dst(buf, blk));
       else
-        load_to_lds(rv, wv.v_dma[i], Vs + buf * C::V_TILE + 1024 * blk);
+        load_to_lds(rv, wv.v_dma[i], v_dst(buf, blk));
     }
   };
   // loads of step p: K tile p+1 and V tile p
@@ -999,21 +1018,42 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     // in fp32, and the range's log2 sum of exp, for the merge.  A row that sees
     // no key of the range (its position lies before the range) has lsum = 0:
     // output 0 and sum -inf, a weight of 0 in the merge.
-    if (my_q < Nq) {
-      const bool seen = lsum > 0.f;
-      const float inv = seen ? sv / lsum : 0.f;
-      const size_t row = (size_t)slot * kBM + (my_q - q0);
-      if (hl == 0) p.ws_lse[row] = seen ? wv.st.m - C::SHIFT + __log2f(lsum) : -INFINITY;
-      float* wo = p.ws_o + row * DV;
+    const bool seen = lsum > 0.f;
+    const float inv = seen ? sv / lsum : 0.f;
+    if (my_q < Nq && hl == 0)
+      p.ws_lse[(size_t)slot * kBM + (my_q - q0)] = seen ? wv.st.m - C::SHIFT + __log2f(lsum) : -INFINITY;
+    // The fp32 rows go out through LDS as the BF16 rows below do (whole rows
+    // per store), in two passes of 16 rows: a wave's 16 rows take 8 KB, 16-byte
+    // chunk c of row r at chunk position c ^ 2r.  The range's rows are
+    // consecutive in the workspace, so each pass stores one contiguous 8 KB.
+    static_assert(DV == 128, "the staging layout holds 512-byte rows");
+    static_assert(C::LDS_BYTES >= kWaves * 16 * DV * 4, "every wave's half rows fit in the tile buffers");
+    uint8_t* const stage = smem + w * (16 * DV * 4);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // addresses computed here (see the BF16 rows below)
+    const int r16 = ln & 15;
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
+    for (int half = 0; half < 2; ++half) {
+      if (((ln >> 4) & 1) == half) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 o4 = {wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv, wv.st.o[d][4 * i + 2] * inv,
-                            wv.st.o[d][4 * i + 3] * inv};
-          *reinterpret_cast<f32x4*>(wo + d * 32 + 8 * i + 4 * hl) = o4;
-        }
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int chunk = 8 * d + 2 * i + (ln >> 5);  // channels 4 chunk .. 4 chunk + 3
+            const f32x4 o4 = {wv.st.o[d][4 * i] * inv, wv.st.o[d][4 * i + 1] * inv, wv.st.o[d][4 * i + 2] * inv,
+                              wv.st.o[d][4 * i + 3] * inv};
+            *reinterpret_cast<f32x4*>(stage + r16 * (DV * 4) + 16 * (chunk ^ (2 * r16))) = o4;
+          }
+      }
+      const int cc = ln & 31;  // the chunk this lane stores
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = 2 * k + (ln >> 5), q = qw0 + 16 * half + row;
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(stage + row * (DV * 4) + 16 * (cc ^ (2 * row)));
+        if (q < Nq) *reinterpret_cast<f32x4*>(p.ws_o + ((size_t)slot * kBM + (q - q0)) * DV + 4 * cc) = v4;
+      }
     }
+    barrier(false);
     return;
   }
   const float inv = sv / lsum;
