@@ -63,7 +63,8 @@
 // (queries) or Nk (keys), and whole tiles past the last one a workgroup needs,
 // load as zeros (buffer bounds), so ragged tiles and the loads of the final
 // steps need no branches; keys >= Nk lie above the diagonal of every valid
-// query and are masked.
+// query and are masked.  At the end of a work item each wave stages its output
+// rows in LDS and stores them from there, four whole rows per instruction.
 //
 // FP8 scale granularity.  Either one fp32 scale per (batch, head) for each of
 // Q, K, V, folded into the score multiplier and the output, or one scale per
