@@ -13,6 +13,10 @@ along every control-flow path into each such load:
   state before it.
 
 An ``s_nop N`` counts N + 1 wait states, any other instruction 1.
+
+A second check reads the same code for spill traffic (scratch accesses, SGPR
+spill lanes) inside each kernel's main loop, where a reload would wait for
+every tile load in flight.
 """
 
 import concurrent.futures as cf
@@ -147,3 +151,52 @@ def test_inline_lds_loads_have_their_wait_states(asm_texts):
                 assert not bad, f"{src} {name}: M0 written directly before '{lines[i]}': {bad[:3]}"
                 checked += 1
     assert checked > 100
+
+
+def _loop_blocks(text: str):
+    """name -> [(loop header of the block or None, [instructions])] for every
+    kernel, from the compiler's loop annotations of the block labels."""
+    kernels = {}
+    for m in re.finditer(r"^(_Z\w*attn_fwd_kernel\w*):.*?$(.*?)^\s*s_endpgm", text, re.S | re.M):
+        blocks, header, ins = [], None, []
+        raw_lines = m.group(2).splitlines()
+        for k, raw in enumerate(raw_lines):
+            s = raw.strip()
+            lab = re.match(r"^(\.LBB(\w+)|; %bb\.\d+):", s)
+            if lab:
+                blocks.append((header, ins))
+                ins = []
+                comment = s + (" " + raw_lines[k + 1].strip() if k + 1 < len(raw_lines) else "")
+                h = re.search(r"in Loop: Header=BB(\w+)", comment)
+                if h:
+                    header = h.group(1)
+                elif "Inner Loop Header" in comment and lab.group(2):
+                    header = lab.group(2)
+                else:
+                    header = None
+                continue
+            ln = raw.split(";")[0].strip()
+            if ln and not ln.startswith("."):
+                ins.append(ln)
+        blocks.append((header, ins))
+        kernels[m.group(1)] = blocks
+    return kernels
+
+
+def test_main_loops_hold_no_spill_traffic(asm_texts):
+    """No scratch access and no SGPR spill lane traffic (v_readlane/v_writelane)
+    inside any kernel's main loop (the innermost loop that issues the MFMAs):
+    a scratch reload there waits for every tile load in flight (the vector
+    memory counter retires in order)."""
+    spill = re.compile(r"^(scratch_|v_readlane_b32|v_writelane_b32)")
+    checked = 0
+    for src, text in asm_texts.items():
+        kernels = _loop_blocks(text)
+        assert kernels, f"no attention kernel found in {src}"
+        for name, blocks in kernels.items():
+            loops = {h for h, ins in blocks if h and any(i.startswith("v_mfma") for i in ins)}
+            assert loops, f"{src} {name}: no loop with MFMAs found"
+            bad = [i for h, ins in blocks if h in loops for i in ins if spill.match(i)]
+            assert not bad, f"{src} {name}: spill traffic in the main loop: {bad[:4]}"
+            checked += 1
+    assert checked >= 20
