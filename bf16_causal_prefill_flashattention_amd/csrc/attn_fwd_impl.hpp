@@ -976,10 +976,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   //   group A: matrix(p) | barrier | vector(p), wait | barrier
   //   group B: matrix(p), wait | barrier | vector(p), loads(p+1) | barrier
   // Group A issues its loads of step p before its matrix work for FP8 and at
-  // the start of its vector work for BF16: the FP8 softmax is at least as long
-  // as its matrix work and the BF16 matrix work is the longer half (the loads take the CU's load path
-  // for a few hundred cycles, so they go where the wave has slack).  Group B
-  // issues at the end of its vector work.  Every load of step p is waited for
+  // the start of its vector work for BF16, group B at the end of its vector
+  // work: the placements that measured fastest (a burst of loads holds the
+  // issuing waves for a few hundred cycles while the CU accepts them).  Every load of step p is waited for
   // at the barrier that ends phase 2p+1, when all waves have issued theirs.
   // No step runs past T, so no loads are issued for one either: an item ends
   // with no load in flight that could land in the next item's first tiles.
