@@ -235,13 +235,25 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const T* x, uint32_t* a
   const int r0 = chunk * kRowsPerBlock;
   const int r1 = min(r0 + kRowsPerBlock, N);
   float m = 0.f;
-  for (int base = r0; base < r1; base += RPP) {  // uniform trip count over the block
-    const int r = base + rr;
-    const bool valid = active && r < r1;
-    const T* row = x + (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
-    float v[NI][8];
+  // Without the rotation, U = 4 passes per round with their loads issued
+  // together: a lane with no row in a pass (past the block's end, or idle)
+  // reads row r0 again instead of reading nothing -- a repeated row leaves the
+  // max unchanged, and the loads then need no branch between them.  With the
+  // rotation (four loads per pass already) a lane with no row loads nothing.
+  constexpr int U = HAD ? 1 : 4;
+  for (int base = r0; base < r1; base += U * RPP) {  // uniform trip count over the block
+    float vu[U][NI][8];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) load8<T>(row + L::ch(cc, i), valid, v[i]);
+    for (int u = 0; u < U; ++u) {
+      const int r = base + u * RPP + rr;
+      const bool valid = active && r < r1;
+      const T* row = x + (((size_t)b * N + (valid ? r : (HAD ? 0 : r0))) * H + h) * D;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) load8<T>(row + L::ch(cc, i), HAD ? valid : true, vu[u][i]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+    float (&v)[NI][8] = vu[u];
     if constexpr (HAD) {
       fwht_row<D, false>(v, sgn1, sgn2);
       constexpr int G = D == 128 ? 2 : 1;  // the last stage pairs groups i and i + G
@@ -257,6 +269,7 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const T* x, uint32_t* a
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+    }
     }
   }
 #pragma unroll
@@ -286,22 +299,55 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const T* x, uint8_t
   const float inv = amax == 0.f ? 1.f : 448.f / amax;
   const int r0 = chunk * kRowsPerBlock;
   const int r1 = min(r0 + kRowsPerBlock, N);
-  for (int base = r0; base < r1; base += RPP) {
-    const int r = base + rr;
-    const bool valid = active && r < r1;
-    const size_t off = (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
-    float v[NI][8];
+  if constexpr (HAD) {
+    for (int base = r0; base < r1; base += RPP) {
+      const int r = base + rr;
+      const bool valid = active && r < r1;
+      const size_t off = (((size_t)b * N + (valid ? r : 0)) * H + h) * D;
+      float v[NI][8];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) load8<T>(x + off + L::ch(cc, i), valid, v[i]);
-    if constexpr (HAD) fwht_row<D, true>(v, sgn1, sgn2);
+      for (int i = 0; i < NI; ++i) load8<T>(x + off + L::ch(cc, i), valid, v[i]);
+      fwht_row<D, true>(v, sgn1, sgn2);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+      for (int i = 0; i < NI; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = fminf(fmaxf(v[i][j] * inv, -448.f), 448.f);
-      if (valid) {
-        i32x2 codes = {(int)pack_fp8x4(v[i][0], v[i][1], v[i][2], v[i][3]),
-                       (int)pack_fp8x4(v[i][4], v[i][5], v[i][6], v[i][7])};
-        *reinterpret_cast<i32x2*>(y + off + L::ch(cc, i)) = codes;
+        for (int j = 0; j < 8; ++j) v[i][j] = fminf(fmaxf(v[i][j] * inv, -448.f), 448.f);
+        if (valid) {
+          i32x2 codes = {(int)pack_fp8x4(v[i][0], v[i][1], v[i][2], v[i][3]),
+                         (int)pack_fp8x4(v[i][4], v[i][5], v[i][6], v[i][7])};
+          *reinterpret_cast<i32x2*>(y + off + L::ch(cc, i)) = codes;
+        }
+      }
+    }
+  } else {
+    // U = 4 passes per round: their loads issued together (a lane with no row
+    // in a pass reads row r0 and stores nothing), then their conversions and
+    // stores
+    constexpr int U = 4;
+    for (int base = r0; base < r1; base += U * RPP) {
+      float vu[U][NI][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = base + u * RPP + rr;
+        const size_t off = (((size_t)b * N + (active && r < r1 ? r : r0)) * H + h) * D;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) load8<T>(x + off + L::ch(cc, i), true, vu[u][i]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = base + u * RPP + rr;
+        const bool valid = active && r < r1;
+        const size_t off = (((size_t)b * N + (valid ? r : r0)) * H + h) * D;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vu[u][i][j] = fminf(fmaxf(vu[u][i][j] * inv, -448.f), 448.f);
+          if (valid) {
+            i32x2 codes = {(int)pack_fp8x4(vu[u][i][0], vu[u][i][1], vu[u][i][2], vu[u][i][3]),
+                           (int)pack_fp8x4(vu[u][i][4], vu[u][i][5], vu[u][i][6], vu[u][i][7])};
+            *reinterpret_cast<i32x2*>(y + off + L::ch(cc, i)) = codes;
+          }
+        }
       }
     }
   }
