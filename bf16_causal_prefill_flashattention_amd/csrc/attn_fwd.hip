@@ -38,7 +38,8 @@ hipError_t device_cus(int* cus) {
 }
 
 int variant_tile_keys(const AttnParams& p, int dtype, int d_qk) {
-  return tile_keys_of(dtype != 0, d_qk, p.block64 != 0, p.p_mode == kPLeanBlock || p.p_mode == kPExactBlock);
+  return tile_keys_of(dtype != 0, d_qk, p.block64 != 0, p.p_mode == kPLeanBlock || p.p_mode == kPExactBlock,
+                      p.Nk <= kShortKeys);
 }
 
 // Key ranges of query tile qt with ranges of L tiles.

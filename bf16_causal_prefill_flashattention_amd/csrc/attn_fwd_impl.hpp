@@ -23,8 +23,9 @@
 //
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
 // (batch, query head); each wave owns 32 queries.  Key tiles hold 192 keys (FP8
-// at d_qk = 128 with per-head scales and no per-64-key shift), 128 (the other
-// FP8 variants), 96 (BF16, d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips
+// at d_qk = 128 with per-head scales and no per-64-key shift, launches of more
+// than 4096 keys), 128 (the other FP8 variants and launches), 96 (BF16,
+// d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips
 // the tiles wholly above its queries and masks only the tiles that cross its
 // diagonal.  A split launch gives each workgroup one range of a query tile's
 // key tiles instead (the kernel's SPLIT instantiation): ranges of a query tile
@@ -119,15 +120,19 @@ constexpr int kBM = kQueryTile;  // queries per workgroup (8 waves x 32)
 
 // Keys per tile.  A phase carries a roughly fixed cost (barriers, the first
 // operand reads), so larger tiles amortise it.  FP8 at d = 128 with one scale
-// per head streams 192-key tiles; 128 where the per-64-key probability shift
+// per head streams 192-key tiles (128 in launches of at most kShortKeys keys,
+// whose last query tiles would waste more of a final 192-key tile); 128 where
+// the per-64-key probability shift
 // (its four max chains) or the per-64-position scale exponents (one word per
 // 128-key tile) assume it, and at d = 192 (192-byte K rows do not split 192
 // keys into whole 1 KB load blocks per wave).  BF16 at d = 128 stops at 96
 // keys (128 would not fit two waves' registers per SIMD); BF16 at d = 192 stays
-// at 64 (its 384-byte K rows would not split into whole blocks at 96).
-template <bool FP8, int DQK, bool BS, int PSH>
+// at 64 (its 384-byte K rows would not split into whole blocks at 96).  SHORT:
+// the variant for launches of at most kShortKeys keys (128-key tiles where the
+// tiles would otherwise hold 192).
+template <bool FP8, int DQK, bool BS, int PSH, bool SHORT = false>
 constexpr int tile_keys() {
-  return tile_keys_of(FP8, DQK, BS, PSH == 1);
+  return tile_keys_of(FP8, DQK, BS, PSH == 1, SHORT);
 }
 
 template <bool FP8, int DQK, int DV, int BN_>
@@ -432,7 +437,7 @@ struct Wave {
 // key order; the order only decides which tiles the workgroups of an XCD read
 // at the same time).  Called by every thread of the workgroup; leaves no load
 // in flight and no wave reading LDS when it returns.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT>
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT>
 __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
                                           bool rev, int ta, int tb, int slot) {
   static_assert(!BS || FP8, "block scales are an FP8 feature");
@@ -441,7 +446,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   static_assert(kShiftStep == 1, "tile_keys names the per-64-key shift by its value");
 
   static_assert(!LEAN || FP8, "lean-P codes are e4m3 codes");
-  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH>()>;
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>()>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
   static_assert(!PS || BN == 128, "the per-64-key shift's four max chains cover two 64-key steps");
@@ -1116,9 +1121,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
 // tiles instead of one stream each.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT>
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
-  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH>()>;
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>()>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
   const int nqt = (p.Nq + kBM - 1) / kBM;
@@ -1138,7 +1143,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       r -= nr;
     }
     const bool multi = (qtile_key_tiles(qt, p.Nq, p.Nk, C::BN) + L - 1) / L > 1;
-    attn_item<DQK, DV, FP8, BS, PSH, LEAN, true>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
+    attn_item<DQK, DV, FP8, BS, PSH, LEAN, true, SHORT>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
                                                  multi ? bh * per_bh + j : -1);
   } else {
     const bool single = (long long)nbh * nqt <= G;  // one tile per unit
@@ -1153,7 +1158,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       const int j = u % per_bh;
       const int qt = half == 0 ? nqt - 1 - j : j;
       if (half == 0 || j != nqt - 1 - j)
-        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false>(p, smem, ebuf, bh, qt, !single && half == 1, 0, 0, -1);
+        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false, SHORT>(p, smem, ebuf, bh, qt, !single && half == 1, 0, 0, -1);
       if (single) {
         u += nrank;
       } else {
@@ -1164,14 +1169,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-// Launch one variant (d_v = 128) on `grid` persistent workgroups.
+// Launch one variant (d_v = 128) on `grid` persistent workgroups: the split
+// instantiation when the launch splits its keys, and the short-sequence tile
+// size where it differs (kShortKeys).
+template <int DQK, bool FP8, bool BS, int PSH, bool LEAN, bool SHORT>
+hipError_t launch_attn_tiles(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.split_tiles > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true, SHORT>), grid, dim3(kThreads), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT>), grid, dim3(kThreads), 0,
+                       stream, p);
+  return hipGetLastError();
+}
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN>
 hipError_t launch_attn_variant(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.split_tiles > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false>), grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (tile_keys<FP8, DQK, BS, PSH, true>() != tile_keys<FP8, DQK, BS, PSH, false>()) {
+    if (p.Nk <= kShortKeys) return launch_attn_tiles<DQK, FP8, BS, PSH, LEAN, true>(p, grid, stream);
+  }
+  return launch_attn_tiles<DQK, FP8, BS, PSH, LEAN, false>(p, grid, stream);
 }
 
 // The probability modes of the FP8 kernels with one scale granularity.

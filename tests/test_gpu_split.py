@@ -28,10 +28,14 @@ pytestmark = pytest.mark.gpu
 QT = 256
 
 
-def tile_keys(fp8, dqk, block64, p_mode):
+SHORT_KEYS = 4096  # launches with at most this many keys use 128-key tiles instead of 192
+
+
+def tile_keys(fp8, dqk, block64, p_mode, Nk):
     if not fp8:
         return 96 if dqk == 128 else 64
-    return 192 if (dqk == 128 and not block64 and p_mode not in ("lean_block", "exact_block")) else 128
+    long_tiles = dqk == 128 and not block64 and p_mode not in ("lean_block", "exact_block") and Nk > SHORT_KEYS
+    return 192 if long_tiles else 128
 
 
 def expected_plan(B, Hq, Nq, Nk, dqk, fp8, block64, p_mode, cus):
@@ -41,7 +45,7 @@ def expected_plan(B, Hq, Nq, Nk, dqk, fp8, block64, p_mode, cus):
     nbh, nqt = B * Hq, (Nq + QT - 1) // QT
     if nbh * nqt > cus:
         return None
-    bn = tile_keys(fp8, dqk, block64, p_mode)
+    bn = tile_keys(fp8, dqk, block64, p_mode, Nk)
     T = [(min((j + 1) * QT, Nq) + Nk - Nq - 1) // bn + 1 for j in range(nqt)]
     ranges = lambda L: [(t + L - 1) // L for t in T]  # noqa: E731
     L0 = next(L for L in range(1, T[-1] + 1) if nbh * sum(ranges(L)) <= cus)
@@ -87,7 +91,8 @@ def _inputs(dtype, B, Nq, Nk, Hq, Hkv, dqk, seed, scales="head", outliers=0):
 
 CASES = [
     # (dtype, B, Nq, Nk, Hq, Hkv, d_qk, scales, p_mode)
-    ("fp8", 1, 2000, 2000, 2, 1, 128, "head", "lean_tile"),  # 192-key tiles, ragged last query tile
+    ("fp8", 1, 2000, 2000, 2, 1, 128, "head", "lean_tile"),  # 128-key tiles (short), ragged last query tile
+    ("fp8", 1, 1200, 5000, 2, 1, 128, "head", "lean_tile"),  # 192-key tiles, ragged, after a key prefix
     ("fp8", 1, 2000, 2000, 2, 2, 128, "head", "exact"),
     ("fp8", 2, 2500, 2500, 1, 1, 192, "head", "lean_tile"),  # MLA shape, 128-key tiles, two sequences
     ("fp8", 1, 1500, 1500, 2, 2, 128, "block64", "lean"),
