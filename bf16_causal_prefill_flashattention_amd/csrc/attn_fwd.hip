@@ -176,6 +176,8 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
   const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.Nq);
+  AttnParams lp = p;
+  lp.solo = 0;
   dim3 grid;
   int first_qt = 0;
   if (p.split_tiles > 0) {
@@ -188,14 +190,23 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
     grid = dim3((unsigned)((long long)p.B * p.Hq * p.split_units));
     first_qt = plan.first_qt;
   } else {
-    // as many workgroups as CUs, or one per tile when the tiles do not fill the
-    // CUs (the kernel derives the same choice from gridDim)
-    grid = dim3(tiles <= cus ? (int)tiles : (int)std::min<long long>(units, cus));
+    const long long solo_items = (long long)p.B * p.Hq * ((p.Nq + kSoloQueryTile - 1) / kSoloQueryTile);
+    if (tiles < cus && solo_items <= cus && p.Nk <= kSoloMaxKeys && variant_tile_keys(p, dtype, d_qk) <= 128) {
+      // 256-query items leave CUs idle and 128-query items fit one per CU:
+      // one 4-wave workgroup per 128-query item (the 4-wave kernels exist for
+      // tiles of at most 128 keys)
+      lp.solo = 1;
+      grid = dim3((unsigned)solo_items);
+    } else {
+      // as many workgroups as CUs, or one per tile when the tiles do not fill
+      // the CUs (the kernel derives the same choice from gridDim)
+      grid = dim3(tiles <= cus ? (int)tiles : (int)std::min<long long>(units, cus));
+    }
   }
-  if (dtype == 0) e = launch_attn_bf16(p, d_qk, grid, stream);
-  else if (p.block64) e = d_qk == 128 ? launch_attn_fp8_block64_d128(p, grid, stream)
-                                      : launch_attn_fp8_block64_d192(p, grid, stream);
-  else e = d_qk == 128 ? launch_attn_fp8_head_d128(p, grid, stream) : launch_attn_fp8_head_d192(p, grid, stream);
+  if (dtype == 0) e = launch_attn_bf16(lp, d_qk, grid, stream);
+  else if (p.block64) e = d_qk == 128 ? launch_attn_fp8_block64_d128(lp, grid, stream)
+                                      : launch_attn_fp8_block64_d192(lp, grid, stream);
+  else e = d_qk == 128 ? launch_attn_fp8_head_d128(lp, grid, stream) : launch_attn_fp8_head_d192(lp, grid, stream);
   if (e != hipSuccess || p.split_tiles == 0) return e;
   const int nqt = (p.Nq + kBM - 1) / kBM;
   const long long mblocks = (long long)p.B * p.Hq * (nqt - first_qt) * (kBM / kMergeRows);

@@ -30,7 +30,9 @@
 // diagonal.  A split launch gives each workgroup one range of a query tile's
 // key tiles instead (the kernel's SPLIT instantiation): ranges of a query tile
 // with more than one write normalised fp32 rows and their log2 sum of exp, and
-// a merge kernel combines them.
+// a merge kernel combines them.  Short launches that leave CUs idle may run
+// 4-wave workgroups over 128 queries instead (NW = 4, one wave per SIMD doing
+// the matrix and the vector work of each step; kSoloQueryTile).
 //
 // Matrix layout.  A wave computes S^T = K_tile * Q^T (keys on MFMA rows,
 // queries on MFMA columns), so lane l owns query (l % 32) and holds half of the
@@ -135,7 +137,7 @@ constexpr int tile_keys() {
   return tile_keys_of(FP8, DQK, BS, PSH == 1, SHORT);
 }
 
-template <bool FP8, int DQK, int DV, int BN_>
+template <bool FP8, int DQK, int DV, int BN_, int NW = 8>
 struct Cfg {
   static constexpr int EB = FP8 ? 1 : 2;     // bytes per element
   static constexpr int BN = BN_;             // keys per tile
@@ -151,15 +153,15 @@ struct Cfg {
   static constexpr int V_TILE = BN * VROW;
   static constexpr int K_BLOCKS = BN * KCH / 64;  // 1 KB LDS-load blocks per K tile
   static constexpr int V_BLOCKS = BN * VCH / 64;
-  static constexpr int K_PER_WAVE = K_BLOCKS / kWaves;
-  static constexpr int V_PER_WAVE = V_BLOCKS / kWaves;
+  static constexpr int K_PER_WAVE = K_BLOCKS / NW;
+  static constexpr int V_PER_WAVE = V_BLOCKS / NW;
   // A wave's consecutive 1 KB load blocks lie kWaves blocks apart.  Where that
   // is a whole number of rows and a multiple of the swizzle period (16 rows),
   // every block of a wave has the same in-tile offset pattern, so one per-lane
   // offset serves all of them and the buffer descriptor moves instead
   // (K: FP8 and BF16 at d = 128; V: always).
-  static constexpr int K_ROWS_STEP = (kWaves * 64) % KCH == 0 ? kWaves * 64 / KCH : 0;
-  static constexpr int V_ROWS_STEP = (kWaves * 64) % VCH == 0 ? kWaves * 64 / VCH : 0;
+  static constexpr int K_ROWS_STEP = (NW * 64) % KCH == 0 ? NW * 64 / KCH : 0;
+  static constexpr int V_ROWS_STEP = (NW * 64) % VCH == 0 ? NW * 64 / VCH : 0;
   static constexpr bool K_UNI = K_ROWS_STEP > 0 && K_ROWS_STEP % 16 == 0;
   static constexpr bool V_UNI = V_ROWS_STEP > 0 && V_ROWS_STEP % 16 == 0;
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
@@ -170,7 +172,7 @@ struct Cfg {
   // finite value (448) for THRESH + SHIFT < 8.855
   static constexpr float THRESH = FP8 ? 2.75f : 8.0f;
   static constexpr float SHIFT = FP8 ? 6.0f : 0.0f;
-  static_assert(K_BLOCKS % kWaves == 0 && V_BLOCKS % kWaves == 0, "tiles split into whole 1 KB blocks per wave");
+  static_assert(K_BLOCKS % NW == 0 && V_BLOCKS % NW == 0, "tiles split into whole 1 KB blocks per wave");
   static_assert(2 * K_TILE <= 65536 && 2 * V_TILE <= 65536, "LDS offsets of a buffer pair fit the 16-bit immediate");
 };
 
@@ -242,11 +244,12 @@ __device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset,
                : "memory");
 }
 // The destination as a generic pointer into the LDS: converted (and
-// null-checked, on its 64 bits) at every load.  The key-split kernel uses the
-// 32-bit form above: with the pointers, the compiler keeps their high words and
-// spills them inside its main loop (each reload then waits for every tile load
-// in flight).  The unsplit kernels keep this form, with which their main loops
-// compile without spills (with the 32-bit form they gain some).
+// null-checked, on its 64 bits) at every load.  The key-split and 4-wave
+// kernels use the 32-bit form above: with the pointers, the compiler keeps their
+// high words and spills them inside its main loop (each reload then waits for
+// every tile load in flight).  The unsplit 8-wave kernels keep this form, with
+// which their main loops compile without spills (with the 32-bit form they gain
+// some).
 __device__ __forceinline__ void load_to_lds(const i32x4& rsrc, uint32_t voffset, const uint8_t* lds_block) {
   load_to_lds(rsrc, voffset, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_block));
 }
@@ -437,7 +440,7 @@ struct Wave {
 // key order; the order only decides which tiles the workgroups of an XCD read
 // at the same time).  Called by every thread of the workgroup; leaves no load
 // in flight and no wave reading LDS when it returns.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT>
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT, int NW>
 __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, uint32_t* ebuf, int bh, int qt,
                                           bool rev, int ta, int tb, int slot) {
   static_assert(!BS || FP8, "block scales are an FP8 feature");
@@ -446,7 +449,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   static_assert(kShiftStep == 1, "tile_keys names the per-64-key shift by its value");
 
   static_assert(!LEAN || FP8, "lean-P codes are e4m3 codes");
-  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>()>;
+  // NW = 8: two wave groups in ping-pong, 256 queries; NW = 4: one wave per
+  // SIMD doing both halves of every step, 128 queries (unsplit launches only)
+  static_assert(NW == 8 || (NW == 4 && !SPLIT), "the key split runs 8-wave workgroups");
+  constexpr bool SOLO = NW == 4;
+  constexpr int kWaves = NW, kThreads = 64 * NW, kBM = 32 * NW;
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>(), NW>;
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
   static_assert(!PS || BN == 128, "the per-64-key shift's four max chains cover two 64-key steps");
@@ -454,29 +462,29 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   static_assert(C::V_TILE % (16 * kThreads) == 0, "the zero-filled V buffer splits into whole stores");
   uint8_t* const Vs = smem;                 // V buffers 0, 1
   uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
-  // the tile loads' destinations (LDS byte addresses in the key-split kernel,
-  // generic pointers otherwise; see load_to_lds)
+  // the tile loads' destinations (LDS byte addresses in the key-split and
+  // 4-wave kernels, generic pointers otherwise; see load_to_lds)
   const uint32_t vs_lds = __builtin_amdgcn_readfirstlane(lds_addr(Vs));
   auto k_dst = [&](int buf, int blk) __attribute__((always_inline)) {
-    if constexpr (SPLIT) return vs_lds + 2 * C::V_TILE + buf * C::K_TILE + 1024 * blk;
+    if constexpr (SPLIT || SOLO) return vs_lds + 2 * C::V_TILE + buf * C::K_TILE + 1024 * blk;
     else return Ks + buf * C::K_TILE + 1024 * blk;
   };
   auto v_dst = [&](int buf, int blk) __attribute__((always_inline)) {
-    if constexpr (SPLIT) return vs_lds + buf * C::V_TILE + 1024 * blk;
+    if constexpr (SPLIT || SOLO) return vs_lds + buf * C::V_TILE + 1024 * blk;
     else return Vs + buf * C::V_TILE + 1024 * blk;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int grp = w >> 2;  // 0: matrix work on even phases, 1: on odd phases
+  const int grp = SOLO ? 0 : w >> 2;  // 0: matrix work on even phases, 1: on odd phases
   const int Nq = p.Nq, Nk = p.Nk;
   const int off = Nk - Nq;  // position of query row 0 in the key sequence
   const int b = bh / p.Hq, h = bh % p.Hq, g = h / (p.Hq / p.Hkv);
   const int q0 = qt * kBM;
   // SIMD s runs waves s (group 0) and s + 4 (group 1); they own query blocks
   // 2s and 2s + 1, so both groups have work on the diagonal tiles.
-  const int qblk = 2 * (w & 3) + grp;
+  const int qblk = SOLO ? w : 2 * (w & 3) + grp;
   const int qw0 = q0 + 32 * qblk;  // first query of this wave
   const int my_q = qw0 + l32;      // query row owned by this lane (position my_q + off)
 
@@ -970,7 +978,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   for (int i = 0; i < (int)(sizeof(wv.pk) / sizeof(wv.pk[0])); ++i) wv.pk[i] = 0u;
   wv.pscale = 0x7f7f7f7fu;  // unit scales
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (grp == 1) {
+  if (!SOLO && grp == 1) {
     issue_step(0);
     barrier(false);  // group B starts one phase later
   }
@@ -1010,11 +1018,30 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
       if (ps + 1 <= NT) step(ps + 1, std::integral_constant<int, 1>{}, group);
     }
   };
-  if (grp == 0)
-    run_steps(std::integral_constant<int, 0>{});
-  else
-    run_steps(std::integral_constant<int, 1>{});
-  if (grp == 0) barrier(false);
+  if constexpr (SOLO) {
+    // One wave per SIMD does the matrix and then the vector work of each step.
+    // The loads of step p (K tile p+1, V tile p) are issued when step p starts,
+    // after the barrier that follows every wave's matrix work of step p-1 (the
+    // last reader of the buffers they fill), and are waited for at the barrier
+    // that starts step p+1.
+    auto solo_step = [&](int ps, auto parity) __attribute__((always_inline)) {
+      if (ps > 0) barrier(true);
+      if (ps < NT) issue_step(ps);
+      matrix_work(ps, parity);
+      vector_work(ps);
+    };
+    for (int ps = 0; ps <= NT; ps += 2) {
+      solo_step(ps, std::integral_constant<int, 0>{});
+      if (ps + 1 <= NT) solo_step(ps + 1, std::integral_constant<int, 1>{});
+    }
+    barrier(false);  // every wave is out of the loop before the epilogue reuses the tile buffers
+  } else {
+    if (grp == 0)
+      run_steps(std::integral_constant<int, 0>{});
+    else
+      run_steps(std::integral_constant<int, 1>{});
+    if (grp == 0) barrier(false);
+  }
 
   // ---- epilogue: normalise by the row sum and store BF16
   const float lsum = PS ? wv.st.l16[0] : (PT ? wv.st.lrun : wv.st.l4[0]);
@@ -1121,12 +1148,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
 // tiles instead of one stream each.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
-  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>()>;
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
+  using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>(), NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
-  const int nqt = (p.Nq + kBM - 1) / kBM;
+  const int nqt = (p.Nq + 32 * NW - 1) / (32 * NW);  // work items of 32 queries per wave
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
   const bool by_xcd = (nbh % 8 == 0) && (G % 8 == 0);
@@ -1143,7 +1170,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       r -= nr;
     }
     const bool multi = (qtile_key_tiles(qt, p.Nq, p.Nk, C::BN) + L - 1) / L > 1;
-    attn_item<DQK, DV, FP8, BS, PSH, LEAN, true, SHORT>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
+    attn_item<DQK, DV, FP8, BS, PSH, LEAN, true, SHORT, NW>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
                                                  multi ? bh * per_bh + j : -1);
   } else {
     const bool single = (long long)nbh * nqt <= G;  // one tile per unit
@@ -1158,7 +1185,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
       const int j = u % per_bh;
       const int qt = half == 0 ? nqt - 1 - j : j;
       if (half == 0 || j != nqt - 1 - j)
-        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false, SHORT>(p, smem, ebuf, bh, qt, !single && half == 1, 0, 0, -1);
+        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false, SHORT, NW>(p, smem, ebuf, bh, qt, !single && half == 1, 0, 0,
+                                                                -1);
       if (single) {
         u += nrank;
       } else {
@@ -1170,16 +1198,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnParams p) {
 }
 
 // Launch one variant (d_v = 128) on `grid` persistent workgroups: the split
-// instantiation when the launch splits its keys, and the short-sequence tile
-// size where it differs (kShortKeys).
+// instantiation when the launch splits its keys, the 4-wave one when the
+// launch runs 128-query items (p.solo), and the short-sequence tile size where
+// it differs (kShortKeys).
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN, bool SHORT>
 hipError_t launch_attn_tiles(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (p.split_tiles > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true, SHORT>), grid, dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true, SHORT, 8>), grid, dim3(512), 0, stream, p);
+  else if constexpr (tile_keys<FP8, DQK, BS, PSH, SHORT>() <= 128) {
+    // (the 4-wave mode exists for tiles of at most 128 keys; the host picks it
+    // only for those)
+    if (p.solo)
+      hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 4>), grid, dim3(256), 0, stream,
+                         p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 8>), grid, dim3(512), 0,
+                         stream, p);
+  } else if (p.solo)
+    return hipErrorInvalidValue;
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT>), grid, dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 8>), grid, dim3(512), 0, stream,
+                       p);
   return hipGetLastError();
 }
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN>

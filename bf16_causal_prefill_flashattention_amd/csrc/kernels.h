@@ -39,12 +39,24 @@ struct AttnParams {
   // bh * split_units + item), and attn_merge_kernel combines the ranges.
   int split_tiles;
   int split_units;
+  // set by launch_attn_fwd: 1 runs 128-query items on 4-wave workgroups (see kSoloQueryTile)
+  int solo;
   float* ws_o;
   float* ws_lse;
 };
 
 // Queries per work item (one workgroup of 8 waves x 32 queries).
 constexpr int kQueryTile = 256;
+// Queries per work item of the 4-wave mode, used by unsplit launches of at
+// most kSoloMaxKeys keys whose 256-query items leave CUs idle while their
+// 128-query items fit one per CU: each wave then does its own matrix and
+// vector work of every step (one wave per SIMD), and twice as many CUs share
+// the launch.  The longest item still walks every key tile, one step per tile
+// as before, and a step of one wave doing both halves takes a little longer
+// than a ping-pong step; what the mode saves is per item (half the queries to
+// load and rows to store), so it pays on short key ranges only.
+constexpr int kSoloQueryTile = 128;
+constexpr int kSoloMaxKeys = 1536;
 
 // Launches with at most this many keys use 128-key FP8 tiles where the kernel
 // would otherwise use 192: a short sequence's last query tile wastes less of
