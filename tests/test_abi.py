@@ -262,3 +262,20 @@ def test_probe_library_exports_its_entry_points():
     lib = ctypes.CDLL(B.PROBE_LIB)
     assert lib.lds_probe_threads() == 256
     assert lib.lds_probe_run(0, 4, 0, 16, None, None) == -1  # rejected before any launch
+
+
+def test_gpu_tests_mirror_the_launch_rules():
+    """The GPU tests that pick shapes by the library's launch rules (the tile
+    size of short launches, the 4-wave mode's key limit) restate those rules;
+    they must match the constants the library is built with."""
+    src = open(os.path.join(ROOT, "bf16_causal_prefill_flashattention_amd", "csrc", "kernels.h")).read()
+
+    def constant(name):
+        return int(re.search(rf"constexpr int {name} = (\d+);", src).group(1))
+
+    tests = os.path.dirname(os.path.abspath(__file__))
+    split = open(os.path.join(tests, "test_gpu_split.py")).read()
+    solo = open(os.path.join(tests, "test_gpu_solo.py")).read()
+    assert int(re.search(r"^SHORT_KEYS = (\d+)", split, re.M).group(1)) == constant("kShortKeys")
+    assert int(re.search(r"^SOLO_MAX_KEYS = (\d+)", solo, re.M).group(1)) == constant("kSoloMaxKeys")
+    assert constant("kSoloQueryTile") == 128 and constant("kQueryTile") == 256
