@@ -166,8 +166,11 @@ def timed_launches(step, steps: int, warmup: int, prewarm_s: float, stream):
     synchronisation and by one pair of HIP events recorded on `stream`, the
     stream the kernels are launched on (events around every launch would let
     the host's enqueue time into short launches' figures).  The clock is
-    sampled throughout.  Returns (wall ms per step, [event ms per step], clock
-    dict)."""
+    sampled throughout.  A second pass of `steps` launches, with an event
+    recorded between consecutive ones, gives the median and the minimum per
+    launch (reported beside the mean of the timed region, not in its place).
+    Returns (wall ms per step, [event ms per step], clock dict with the median
+    and minimum)."""
     import torch
 
     with ClockSampler() as clk:
@@ -189,9 +192,18 @@ def timed_launches(step, steps: int, warmup: int, prewarm_s: float, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    median = per[steps // 2] if steps % 2 else (per[steps // 2 - 1] + per[steps // 2]) / 2
     sclk, n = clk.mean(t0, t1)
     sclk_pre, npre = clk.mean((tp0 + tp1) / 2, tp1)
-    clock = {"sclk_mhz": sclk, "sclk_samples": n, "sclk_prewarm_mhz": sclk_pre, "prewarm_s": round(tp1 - tp0, 2)}
+    clock = {"sclk_mhz": sclk, "sclk_samples": n, "sclk_prewarm_mhz": sclk_pre, "prewarm_s": round(tp1 - tp0, 2),
+             "launch_ms_median": round(median, 4), "launch_ms_min": round(per[0], 4)}
     return (t1 - t0) * 1e3 / steps, [e0.elapsed_time(e1) / steps], clock
 
 
@@ -649,6 +661,9 @@ def main(argv=None):
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path is a single-GPU kernel and the library has no "
               "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         return 2
     if args.clock_study:
         return clock_study(args.study_seconds)
