@@ -26,7 +26,11 @@ has settled when the timed region starts.  ``sclk_mhz`` is the graphics clock
 sampled (amdsmi, every 10 ms) during the timed region, ``sclk_prewarm_mhz`` the
 same over the second half of the pre-warm, and ``frac_at_sclk`` the fraction of
 the peak scaled from its 2.4 GHz to the timed region's clock (the random
-operand data holds the clock below 2.4 GHz).
+operand data holds the clock below 2.4 GHz).  ``launch_ms_median`` and
+``launch_ms_min`` come from a second pass of as many launches with an event
+between consecutive ones.  ``determinism``: after each leg's timed launches,
+``--determinism`` (default 100) more launches on the same inputs, each compared
+bit for bit with the output (and, for the chunk, the LSE) of the timed ones.
 
 ``cpu_baseline`` times the CPU oracle (test infrastructure, untuned) on a
 bounded sample of the same workload: whole heads, every row, one head per
@@ -40,7 +44,7 @@ the oracle quantizer's.  The BF16 leg gets its own ``parity`` the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--prewarm SECONDS] [--no-bf16] [--no-cpu-baseline]
-                       [--no-chunk] [--no-block64]
+                       [--no-chunk] [--no-block64] [--determinism N]
        python bench.py --clock-study [--study-seconds S]
 
 ``--clock-study`` measures how the input data and the FP8 probability mode
@@ -207,7 +211,26 @@ def timed_launches(step, steps: int, warmup: int, prewarm_s: float, stream):
     return (t1 - t0) * 1e3 / steps, [e0.elapsed_time(e1) / steps], clock
 
 
-def run_gpu(w, steps: int, warmup: int, prewarm_s: float):
+def determinism_pass(step, outs, launches: int):
+    """`launches` more calls of `step` on the same inputs after the timed ones;
+    each must reproduce the tensors in `outs` (as the timed launches left them)
+    bit for bit, compared as raw integers (so -0 against +0 or a NaN payload
+    would count as a difference).  None when launches is 0."""
+    import torch
+
+    if launches <= 0:
+        return None
+    ints = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+    refs = [t.view(ints[t.element_size()]).clone() for t in outs]
+    equal = 0
+    for _ in range(launches):
+        step()
+        equal += all(torch.equal(t.view(ints[t.element_size()]), r) for t, r in zip(outs, refs))
+    return {"launches": launches, "bitwise_equal": int(equal), "pass": equal == launches,
+            "reference": "the output of the timed launches"}
+
+
+def run_gpu(w, steps: int, warmup: int, prewarm_s: float, determinism: int = 0):
     """Time `steps` attention launches of workload w on inputs resident in HBM.
     Returns a dict: wall ms per step, per-launch event ms, front-end ms (FP8),
     clock readings, and on the host the output of the timed launches, the BF16
@@ -266,7 +289,8 @@ def run_gpu(w, steps: int, warmup: int, prewarm_s: float):
     step, _, _ = miattn.attn_fwd_ws_bind(*args, out=out, with_lse=False, scales=scales, p_mode=p_mode)
 
     ms, attn_ms, clock = timed_launches(step, steps, warmup, prewarm_s, stream)
-    return {"ms": ms, "attn_ms": attn_ms, "front_ms": front_ms, "clock": clock,
+    det = determinism_pass(step, [out], determinism)
+    return {"ms": ms, "attn_ms": attn_ms, "front_ms": front_ms, "clock": clock, "determinism": det,
             "out": out.cpu(), "inputs": (hq, hk, hv), "codes": codes}
 
 
@@ -345,10 +369,11 @@ def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
     return float(B) * Hq * (2.0 * Nq * Nk - float(Nq) ** 2) * (d_qk + d_v)
 
 
-def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float):
+def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float, determinism: int = 0):
     """Time attn_fwd_chunk (with LSE) for the last Nq positions of workload w's
     FP8 sequence; inputs quantized by the library and resident in HBM.
-    Returns (wall ms per step, per-launch event ms, clock dict)."""
+    Returns (wall ms per step, per-launch event ms, clock dict, determinism
+    record of output and LSE)."""
     import torch
 
     import bf16_causal_prefill_flashattention_amd as miattn
@@ -367,7 +392,8 @@ def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float):
     def step():
         miattn.attn_fwd_chunk(cq, ck, cv, sq, sk, sv, out=out, lse=lse)
 
-    return timed_launches(step, steps, warmup, prewarm_s, stream)
+    ms, attn_ms, clock = timed_launches(step, steps, warmup, prewarm_s, stream)
+    return ms, attn_ms, clock, determinism_pass(step, [out, lse], determinism)
 
 
 PEAK_SCLK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
@@ -654,6 +680,9 @@ def main(argv=None):
                          "for reading the LDS bank-conflict counter against them under rocprofv3 --pmc")
     ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
+    ap.add_argument("--determinism", type=int, default=100,
+                    help="after each leg's timed launches, this many more launches on the same inputs, each "
+                         "checked bit for bit against the timed launches' output (0: none)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the warmup, run one plain elementwise copy (torch.neg) that reads and writes "
                          "this many bytes: the reference kernel of known traffic for scaling HBM counters")
@@ -662,8 +691,8 @@ def main(argv=None):
         print("bench.py measures one GPU only: the path is a single-GPU kernel and the library has no "
               "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.determinism < 0:
+        print("--steps must be at least 1, --warmup and --determinism at least 0", file=sys.stderr)
         return 2
     if args.clock_study:
         return clock_study(args.study_seconds)
@@ -701,7 +730,7 @@ def bench(args, w, WORKLOADS, pool):
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    res = run_gpu(w, args.steps, args.warmup, args.prewarm)
+    res = run_gpu(w, args.steps, args.warmup, args.prewarm, args.determinism)
     ms = res["ms"]
     value = w.causal_flops / (ms * 1e-3) / 1e12
     rec = {
@@ -724,6 +753,7 @@ def bench(args, w, WORKLOADS, pool):
             "step": "one attn_fwd_ws call: one attention launch (launches that split their keys add a merge kernel)",
         },
         "roofline": roofline(w, res["attn_ms"], clock=res["clock"]),
+        "determinism": res["determinism"],
     }
     if res["front_ms"] is not None:
         rec["front_end"] = {"what": "quantize Q, K, V (bf16 -> e4m3, per-head amax/448), timed apart from the metric",
@@ -733,19 +763,20 @@ def bench(args, w, WORKLOADS, pool):
     del res
     if not args.no_bf16 and w.dtype == "fp8":
         wb = WORKLOADS[args.bf16_workload]
-        rb = run_gpu(wb, args.steps, args.warmup, args.prewarm)
+        rb = run_gpu(wb, args.steps, args.warmup, args.prewarm, args.determinism)
         rec["bf16"] = {
             "workload": wb.name,
             "value": round(wb.causal_flops / (rb["ms"] * 1e-3) / 1e12, 1),
             "ms_per_step": round(rb["ms"], 4),
             "roofline": roofline(wb, rb["attn_ms"], clock=rb["clock"]),
+            "determinism": rb["determinism"],
         }
         if pool is not None:
             rec["bf16"]["parity"] = oracle_heads(pool, wb, rb)[0]
         del rb
     if not args.no_block64 and w.name == "fp8_mha_n32k":
         wq = WORKLOADS["fp8_mha_n32k_block64"]
-        rq = run_gpu(wq, args.steps, args.warmup, args.prewarm)
+        rq = run_gpu(wq, args.steps, args.warmup, args.prewarm, args.determinism)
         rec["block64"] = {
             "workload": f"{wq.name}: the same inputs with one power-of-two scale per 64 positions "
                         "(K and V scales applied by the scaled MFMAs)",
@@ -753,20 +784,22 @@ def bench(args, w, WORKLOADS, pool):
             "ms_per_step": round(rq["ms"], 4),
             "front_end_ms": round(rq["front_ms"], 4),
             "roofline": roofline(wq, rq["attn_ms"], clock=rq["clock"]),
+            "determinism": rq["determinism"],
         }
         del rq
         wp = WORKLOADS["fp8_mha_n32k_block64_pscale"]
-        rp = run_gpu(wp, args.steps, args.warmup, args.prewarm)
+        rp = run_gpu(wp, args.steps, args.warmup, args.prewarm, args.determinism)
         rec["block64"]["p_block_scale"] = {
             "workload": f"{wp.name}: probabilities also scaled per block by powers of two",
             "value": round(wp.causal_flops / (rp["ms"] * 1e-3) / 1e12, 1),
             "ms_per_step": round(rp["ms"], 4),
             "roofline": roofline(wp, rp["attn_ms"], clock=rp["clock"]),
+            "determinism": rp["determinism"],
         }
         del rp
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
-        msc, attn_c, clock_c = run_chunk(w, Nq, args.steps, args.warmup, args.prewarm)
+        msc, attn_c, clock_c, det_c = run_chunk(w, Nq, args.steps, args.warmup, args.prewarm, args.determinism)
         fl = chunk_flops(w.B, w.Hq, Nq, w.N, w.d_qk, w.d_v)
         rec["chunk"] = {
             "workload": f"{w.name} chunk: last {Nq} positions against {w.N} keys, LSE written",
@@ -774,6 +807,7 @@ def bench(args, w, WORKLOADS, pool):
             "value": round(fl / (msc * 1e-3) / 1e12, 1),
             "ms_per_step": round(msc, 4),
             "roofline": roofline(w, attn_c, fl, clock=clock_c),
+            "determinism": det_c,
         }
         rec["chunk"]["roofline"]["traffic"] = None
     rec["kernel_source_hash"] = kernel_source_hash()
