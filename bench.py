@@ -44,7 +44,7 @@ the oracle quantizer's.  The BF16 leg gets its own ``parity`` the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--prewarm SECONDS] [--no-bf16] [--no-cpu-baseline]
-                       [--no-chunk] [--no-block64] [--determinism N]
+                       [--no-chunk] [--no-block64] [--determinism N] [--p-mode MODE]
        python bench.py --clock-study [--study-seconds S]
 
 ``--clock-study`` measures how the input data and the FP8 probability mode
@@ -230,7 +230,7 @@ def determinism_pass(step, outs, launches: int):
             "reference": "the output of the timed launches"}
 
 
-def run_gpu(w, steps: int, warmup: int, prewarm_s: float, determinism: int = 0):
+def run_gpu(w, steps: int, warmup: int, prewarm_s: float, determinism: int = 0, p_mode=None):
     """Time `steps` attention launches of workload w on inputs resident in HBM.
     Returns a dict: wall ms per step, per-launch event ms, front-end ms (FP8),
     clock readings, and on the host the output of the timed launches, the BF16
@@ -285,7 +285,7 @@ def run_gpu(w, steps: int, warmup: int, prewarm_s: float, determinism: int = 0):
     # that leave compute units idle split their keys), checked and marshalled
     # once; the workspace is allocated here, outside the timed launches
     scales = "block64" if block64 else "head"
-    p_mode = ("lean_block" if w.p_block_scale else "lean") if block64 else miattn.DEFAULT_P_MODE
+    p_mode = ("lean_block" if w.p_block_scale else "lean") if block64 else (p_mode or miattn.DEFAULT_P_MODE)
     step, _, _ = miattn.attn_fwd_ws_bind(*args, out=out, with_lse=False, scales=scales, p_mode=p_mode)
 
     ms, attn_ms, clock = timed_launches(step, steps, warmup, prewarm_s, stream)
@@ -369,7 +369,7 @@ def chunk_flops(B, Hq, Nq, Nk, d_qk, d_v) -> float:
     return float(B) * Hq * (2.0 * Nq * Nk - float(Nq) ** 2) * (d_qk + d_v)
 
 
-def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float, determinism: int = 0):
+def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float, determinism: int = 0, p_mode=None):
     """Time attn_fwd_chunk (with LSE) for the last Nq positions of workload w's
     FP8 sequence; inputs quantized by the library and resident in HBM.
     Returns (wall ms per step, per-launch event ms, clock dict, determinism
@@ -390,7 +390,10 @@ def run_chunk(w, Nq: int, steps: int, warmup: int, prewarm_s: float, determinism
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        miattn.attn_fwd_chunk(cq, ck, cv, sq, sk, sv, out=out, lse=lse)
+        if p_mode is None:  # the library's default probability mode
+            miattn.attn_fwd_chunk(cq, ck, cv, sq, sk, sv, out=out, lse=lse)
+        else:
+            miattn.attn_fwd_fp8(cq, ck, cv, sq, sk, sv, out=out, lse=lse, p_mode=p_mode)
 
     ms, attn_ms, clock = timed_launches(step, steps, warmup, prewarm_s, stream)
     return ms, attn_ms, clock, determinism_pass(step, [out, lse], determinism)
@@ -680,6 +683,9 @@ def main(argv=None):
                          "for reading the LDS bank-conflict counter against them under rocprofv3 --pmc")
     ap.add_argument("--study-seconds", type=float, default=3.0)
     ap.add_argument("--chunk-queries", type=int, default=8192)
+    ap.add_argument("--p-mode", default=None,
+                    help="FP8 probability mode of the per-head FP8 leg and the chunk (lean, lean_block, lean_tile, "
+                         "exact, exact_block, exact_tile; default: the library's default)")
     ap.add_argument("--determinism", type=int, default=100,
                     help="after each leg's timed launches, this many more launches on the same inputs, each "
                          "checked bit for bit against the timed launches' output (0: none)")
@@ -694,6 +700,12 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0 or args.determinism < 0:
         print("--steps must be at least 1, --warmup and --determinism at least 0", file=sys.stderr)
         return 2
+    if args.p_mode is not None:
+        from bf16_causal_prefill_flashattention_amd import P_MODES
+
+        if args.p_mode not in P_MODES:
+            print(f"--p-mode must be one of {sorted(P_MODES)}", file=sys.stderr)
+            return 2
     if args.clock_study:
         return clock_study(args.study_seconds)
     if args.lds_probe:
@@ -720,6 +732,8 @@ def main(argv=None):
 def bench(args, w, WORKLOADS, pool):
     import torch
 
+    from bf16_causal_prefill_flashattention_amd import DEFAULT_P_MODE
+
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -730,7 +744,7 @@ def bench(args, w, WORKLOADS, pool):
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    res = run_gpu(w, args.steps, args.warmup, args.prewarm, args.determinism)
+    res = run_gpu(w, args.steps, args.warmup, args.prewarm, args.determinism, args.p_mode)
     ms = res["ms"]
     value = w.causal_flops / (ms * 1e-3) / 1e12
     rec = {
@@ -750,6 +764,7 @@ def bench(args, w, WORKLOADS, pool):
         "config": {
             "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d_qk": w.d_qk, "d_v": w.d_v,
             "outlier_channels": w.outliers, "hadamard": w.hadamard,
+            **({"p_mode": args.p_mode or DEFAULT_P_MODE} if w.dtype == "fp8" and w.scales == "head" else {}),
             "step": "one attn_fwd_ws call: one attention launch (launches that split their keys add a merge kernel)",
         },
         "roofline": roofline(w, res["attn_ms"], clock=res["clock"]),
@@ -799,7 +814,8 @@ def bench(args, w, WORKLOADS, pool):
         del rp
     if not args.no_chunk and w.dtype == "fp8" and 0 < args.chunk_queries <= w.N:
         Nq = args.chunk_queries
-        msc, attn_c, clock_c, det_c = run_chunk(w, Nq, args.steps, args.warmup, args.prewarm, args.determinism)
+        msc, attn_c, clock_c, det_c = run_chunk(w, Nq, args.steps, args.warmup, args.prewarm, args.determinism,
+                                                args.p_mode)
         fl = chunk_flops(w.B, w.Hq, Nq, w.N, w.d_qk, w.d_v)
         rec["chunk"] = {
             "workload": f"{w.name} chunk: last {Nq} positions against {w.N} keys, LSE written",
