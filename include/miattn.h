@@ -75,8 +75,10 @@ extern "C" {
  * enqueued), Hq >= 1, Hkv >= 1, Hq % Hkv == 0, (d_qk, d_v) in
  * {(128, 128), (192, 128)}.  Any N is accepted (ragged tails are masked).
  * stream: a hipStream_t, or NULL for the default stream.
- * The result is bitwise reproducible from launch to launch (no atomics, fixed
- * reduction order).
+ * The result is bitwise reproducible from launch to launch on one device (no
+ * atomics, fixed reduction order); the order in which a query row meets its
+ * key tiles follows the work schedule, which depends on the device's compute
+ * unit count, so another device may differ in the last bits.
  * Returns MIATTN_OK or a negative MIATTN_ERR_* code. */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d_qk,
              int d_v, int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* stream);
