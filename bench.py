@@ -73,7 +73,8 @@ if ROOT not in sys.path:
 METRIC = "causal attn fwd TFLOP/s (FP8 & BF16, d=128, N=32K) + % of MFMA peak"
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense MFMA, published
 PAGES_FP8_HD128_32K = 2672.0  # TFLOP/s, FP8 causal fwd, hd128, N=32K, Gaussian, on MI355X (the pages' figure)
-ATTN_KERNEL_SOURCES = ["attn_fwd_impl.hpp", "device_common.hpp"]  # the kernel template and its helpers
+# the kernel template, its helpers, the tile-size rules and the launch logic that picks the variant and grid
+ATTN_KERNEL_SOURCES = ["attn_fwd_impl.hpp", "device_common.hpp", "kernels.h", "attn_fwd.hip"]
 
 
 def code_tokens(text: str) -> str:

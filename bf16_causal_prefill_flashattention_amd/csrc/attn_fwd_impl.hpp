@@ -24,7 +24,7 @@
 // Work decomposition.  One workgroup = 8 waves = 256 consecutive queries of one
 // (batch, query head); each wave owns 32 queries.  Key tiles hold 192 keys (FP8
 // at d_qk = 128 with per-head scales and no per-64-key shift, launches of more
-// than 4096 keys), 128 (the other FP8 variants and launches), 96 (BF16,
+// than 4096 keys), 128 (the other FP8 variants and launches, and BF16 at
 // d_qk = 128) or 64 (BF16, d_qk = 192); a wave skips
 // the tiles wholly above its queries and masks only the tiles that cross its
 // diagonal.  A split launch gives each workgroup one range of a query tile's
@@ -127,9 +127,10 @@ constexpr int kBM = kQueryTile;  // queries per workgroup (8 waves x 32)
 // the per-64-key probability shift
 // (its four max chains) or the per-64-position scale exponents (one word per
 // 128-key tile) assume it, and at d = 192 (192-byte K rows do not split 192
-// keys into whole 1 KB load blocks per wave).  BF16 at d = 128 stops at 96
-// keys (128 would not fit two waves' registers per SIMD); BF16 at d = 192 stays
-// at 64 (its 384-byte K rows would not split into whole blocks at 96).  SHORT:
+// keys into whole 1 KB load blocks per wave).  BF16 at d = 128 streams 128
+// keys (its two 32 KB buffers of K and of V fill 128 KB of LDS, and 192 would
+// not fit it); BF16 at d = 192 stays at 64 (its 384-byte K rows would not
+// split into whole blocks at 96, and 128 would take all 160 KB).  SHORT:
 // the variant for launches of at most kShortKeys keys (128-key tiles where the
 // tiles would otherwise hold 192).
 template <bool FP8, int DQK, bool BS, int PSH, bool SHORT = false>

@@ -33,7 +33,7 @@ SHORT_KEYS = 4096  # launches with at most this many keys use 128-key tiles inst
 
 def tile_keys(fp8, dqk, block64, p_mode, Nk):
     if not fp8:
-        return 96 if dqk == 128 else 64
+        return 128 if dqk == 128 else 64
     long_tiles = dqk == 128 and not block64 and p_mode not in ("lean_block", "exact_block") and Nk > SHORT_KEYS
     return 192 if long_tiles else 128
 
@@ -99,7 +99,7 @@ CASES = [
     ("fp8", 1, 1500, 1500, 2, 2, 128, "block64", "lean_block"),
     ("fp8", 1, 300, 9000, 4, 1, 128, "head", "lean_tile"),  # short chunk, long prefix
     ("fp8", 1, 1, 5000, 2, 2, 128, "head", "exact_tile"),  # one query
-    ("bf16", 1, 1800, 1800, 2, 1, 128, "head", "lean"),  # 96-key tiles
+    ("bf16", 1, 1800, 1800, 2, 1, 128, "head", "lean"),  # 128-key tiles
     ("bf16", 1, 1000, 1000, 2, 2, 192, "head", "lean"),  # 64-key tiles
     ("bf16", 1, 256, 6000, 8, 8, 128, "head", "lean"),
 ]
