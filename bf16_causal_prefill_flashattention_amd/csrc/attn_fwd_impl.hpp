@@ -459,7 +459,13 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   constexpr int NBLK = C::NBLK;
   constexpr int BN = C::BN;
   static_assert(!PS || BN == 128, "the per-64-key shift's four max chains cover two 64-key steps");
-  static_assert(!BS || BN == 128, "block-scale exponents are staged one word per 128-key tile");
+  static_assert(!BS || BN == 128 || BN == 192, "block-scale exponents are staged per 128- or 192-key tile");
+  // block scales: ebuf words per tile (128 keys: one word, K and V exponents
+  // of its two 64-key blocks; 192 keys: a K word and a V word, three blocks
+  // each), and the byte of a V word that holds the exponent of P.V k-step 0
+  constexpr int EW = BS && BN == 192 ? 2 : 1;
+  constexpr int VSEL = BS && BN == 192 ? 0 : 2;
+  constexpr bool V3 = BS && BN == 192;  // a third P.V k-step reads V byte 2
   static_assert(C::V_TILE % (16 * kThreads) == 0, "the zero-filled V buffer splits into whole stores");
   uint8_t* const Vs = smem;                 // V buffers 0, 1
   uint8_t* const Ks = smem + 2 * C::V_TILE;  // K buffers 0, 1
@@ -732,13 +738,16 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
         } else if constexpr (PT) {
           // the step's row sum on its own (scaled back when the phase ends)
           if (db == 0) rs = mfma_fp8_16x16x128(sel, pb, ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : rs);
-          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
-                                : mfma_fp8_32x32x64_sab<3, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale);
+          wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sab<VSEL, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
+                        : (V3 && ks == 2) ? mfma_fp8_32x32x64_sab<2, 0>(a, pb, wv.st.o[db], (int)vexp, (int)wv.pscale)
+                                                  : mfma_fp8_32x32x64_sab<VSEL + 1, 0>(a, pb, wv.st.o[db], (int)vexp,
+                                                                                      (int)wv.pscale);
         } else {
           if (db == 0) wv.st.l4 = mfma_fp8_16x16x128(sel, pb, wv.st.l4);
           if constexpr (BS)
-            wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
-                                  : mfma_fp8_32x32x64_sa<3>(a, pb, wv.st.o[db], (int)vexp);
+            wv.st.o[db] = ks == 0 ? mfma_fp8_32x32x64_sa<VSEL>(a, pb, wv.st.o[db], (int)vexp)
+                          : (V3 && ks == 2) ? mfma_fp8_32x32x64_sa<2>(a, pb, wv.st.o[db], (int)vexp)
+                                                    : mfma_fp8_32x32x64_sa<VSEL + 1>(a, pb, wv.st.o[db], (int)vexp);
           else
             wv.st.o[db] = mfma_fp8_32x32x64(a, pb, wv.st.o[db]);
         }
@@ -756,7 +765,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
       const f32x16 acc = kk == 0 ? zero16() : wv.s[blk];
       if constexpr (FP8 && BS)
         wv.s[blk] = blk < 2 ? mfma_fp8_32x32x64_sa<0>(a, wv.q[kk], acc, (int)kexp)
-                            : mfma_fp8_32x32x64_sa<1>(a, wv.q[kk], acc, (int)kexp);
+                    : blk < 4 ? mfma_fp8_32x32x64_sa<1>(a, wv.q[kk], acc, (int)kexp)
+                              : mfma_fp8_32x32x64_sa<2>(a, wv.q[kk], acc, (int)kexp);
       else if constexpr (FP8)
         wv.s[blk] = mfma_fp8_32x32x64(a, wv.q[kk], acc);
       else
@@ -799,8 +809,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
     if (pstep >= s_lo && pstep <= s_hi) {
       sel = selector();
       if constexpr (BS) {
-        kexp = ebuf[tile_of(pstep)];
-        vexp = ebuf[tile_of(pstep - 1)];
+        kexp = ebuf[EW * tile_of(pstep)];
+        vexp = ebuf[EW * tile_of(pstep - 1) + EW - 1];
       }
       run_ops(std::integral_constant<int, 0>{}, std::integral_constant<int, PV_OPS + QK_OPS>{}, vb, kb);
       // shift per tile: the row sum of the probabilities just multiplied (they
@@ -958,17 +968,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
   // into buffer 0; V buffer 1 (read by the empty P.V product of step 0) and the
   // probabilities start at zero.
   if constexpr (BS) {
-    // word t: E8M0 of K blocks 2t, 2t+1 and V blocks 2t, 2t+1 (indices past the
-    // last block repeat it: those keys load as zeros and are masked)
+    // 128-key tiles: word t = E8M0 of K blocks 2t, 2t+1 and V blocks 2t, 2t+1;
+    // 192-key tiles: word 2t = K blocks 3t .. 3t+2, word 2t+1 = V blocks 3t ..
+    // 3t+2 (indices past the last block repeat it: those keys load as zeros and
+    // are masked)
     const int nbk = (Nk + 63) / 64;
     const float* ksc = p.k_scale + ((size_t)b * p.Hkv + g) * nbk;
     const float* vsc = p.v_scale + ((size_t)b * p.Hkv + g) * nbk;
+    auto e8 = [](float x) __attribute__((always_inline)) { return (__float_as_uint(x) >> 23) & 0xffu; };
     for (int t = tid; t <= T; t += kThreads) {
-      const int i0 = min(2 * t, nbk - 1), i1 = min(2 * t + 1, nbk - 1);
-      const uint32_t k0 = __float_as_uint(ksc[i0]), k1 = __float_as_uint(ksc[i1]);
-      const uint32_t v0 = __float_as_uint(vsc[i0]), v1 = __float_as_uint(vsc[i1]);
-      ebuf[t] = ((k0 >> 23) & 0xffu) | (((k1 >> 23) & 0xffu) << 8) | (((v0 >> 23) & 0xffu) << 16) |
-                (((v1 >> 23) & 0xffu) << 24);
+      if constexpr (BN == 192) {
+        const int i0 = min(3 * t, nbk - 1), i1 = min(3 * t + 1, nbk - 1), i2 = min(3 * t + 2, nbk - 1);
+        ebuf[2 * t] = e8(ksc[i0]) | (e8(ksc[i1]) << 8) | (e8(ksc[i2]) << 16);
+        ebuf[2 * t + 1] = e8(vsc[i0]) | (e8(vsc[i1]) << 8) | (e8(vsc[i2]) << 16);
+      } else {
+        const int i0 = min(2 * t, nbk - 1), i1 = min(2 * t + 1, nbk - 1);
+        ebuf[t] = e8(ksc[i0]) | (e8(ksc[i1]) << 8) | (e8(vsc[i0]) << 16) | (e8(vsc[i1]) << 24);
+      }
     }
   }
   issue_k(tile_of(0), 0);
@@ -1153,7 +1169,7 @@ template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bo
 __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>(), NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-  __shared__ uint32_t ebuf[BS ? kBlock64MaxKeys / C::BN + 1 : 1];
+  __shared__ uint32_t ebuf[BS ? (C::BN == 192 ? 2 : 1) * (kBlock64MaxKeys / C::BN + 1) : 1];
   const int nqt = (p.Nq + 32 * NW - 1) / (32 * NW);  // work items of 32 queries per wave
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;

@@ -64,12 +64,13 @@ constexpr int kSoloMaxKeys = 1536;
 // 128, 16K and 32K 2-4% slower).
 constexpr int kShortKeys = 4096;
 
-// Keys per tile of a kernel variant: FP8 at d_qk = 128 with one scale per head
-// and no per-64-key probability shift streams 192-key tiles (128 when the
-// launch has at most kShortKeys keys), the other FP8 variants 128; BF16 128 at
-// d_qk = 128 and 64 at d_qk = 192.
+// Keys per tile of a kernel variant: FP8 at d_qk = 128 without the per-64-key
+// probability shift streams 192-key tiles (128 when the launch has at most
+// kShortKeys keys), the other FP8 variants 128; BF16 128 at d_qk = 128 and 64
+// at d_qk = 192.  (block64: the scale granularity, which does not change it.)
 constexpr int tile_keys_of(bool fp8, int d_qk, bool block64, bool shift_step, bool short_keys = false) {
-  return fp8 ? ((d_qk == 128 && !block64 && !shift_step && !short_keys) ? 192 : 128) : (d_qk == 128 ? 128 : 64);
+  (void)block64;
+  return fp8 ? ((d_qk == 128 && !shift_step && !short_keys) ? 192 : 128) : (d_qk == 128 ? 128 : 64);
 }
 
 // Key tiles query tile qt needs: keys up to the position of its last query.

@@ -229,8 +229,8 @@ int attn_fwd_block64(const void* q, const void* k, const void* v, void* out, flo
 #define MIATTN_P_EXACT 2       /* exp2 and the hardware round-to-nearest-even e4m3 conversion */
 #define MIATTN_P_EXACT_BLOCK 3 /* exact, with the per-64-key shift of MIATTN_P_LEAN_BLOCK */
 #define MIATTN_P_LEAN_TILE 4   /* lean P, and each query's probabilities of every key tile (192
-                                  keys at d_qk = 128 with per-head scales and more than 4096
-                                  keys, else 128) shifted up by
+                                  keys at d_qk = 128 in launches of more than 4096 keys, else
+                                  128) shifted up by
                                   2^k (k = min(floor(running max - their max), 126)); the scaled
                                   MFMAs multiply them by 2^-k */
 #define MIATTN_P_EXACT_TILE 5  /* exact, with the per-tile shift of MIATTN_P_LEAN_TILE */

@@ -164,18 +164,19 @@ def test_block64_scales_are_applied(require_gpu):
     assert e_b <= TOL["fp8"] and e_h > 0.2 and e_b < 0.25 * e_h, (e_b, e_h)
 
 
-# (d_qk, probability mode) pairs whose per-head and block-scaled kernels stream
-# tiles of the same size at the test's 900 keys (128 keys; the per-head kernel at
-# d = 128 streams 192-key tiles only beyond 4096 keys)
-SAME_TILES = [(d, m) for d in (128, 192) for m in sorted(miattn.P_MODES)]
+# (d_qk, probability mode, keys): the per-head and block-scaled kernels follow
+# one tile rule (128 keys at 900; beyond 4096 keys at d = 128, 192 without the
+# per-64-key shift), so they stream tiles of the same size in every case
+SAME_TILES = [(d, m, 900) for d in (128, 192) for m in sorted(miattn.P_MODES)] + \
+    [(128, m, 5000) for m in sorted(miattn.P_MODES)]
 
 
-@pytest.mark.parametrize("dqk,mode", SAME_TILES)
-def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk, mode):
+@pytest.mark.parametrize("dqk,mode,Nk", SAME_TILES)
+def test_uniform_power_of_two_blocks_reproduce_per_head_kernel(require_gpu, dqk, mode, Nk):
     """Every block scale of a head equal to one power of two: the block-scaled
     kernel gives the per-head kernel's bits (a power-of-two scale inside the
     MFMA commutes with every rounding), with the same tile size and mode."""
-    B, Nq, Nk, Hq, Hkv = 1, 500, 900, 4, 2
+    B, Nq, Hq, Hkv = 1, 500, 4, 2
     g = np.random.default_rng(dqk)
     codes = [g.integers(0, 256, size=s, dtype=np.uint8) for s in
              ((B, Nq, Hq, dqk), (B, Nk, Hkv, dqk), (B, Nk, Hkv, 128))]

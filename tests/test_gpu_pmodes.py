@@ -61,6 +61,7 @@ CASES = [
     (2, 300, 1000, 4, 4, 128, 0),
     (1, 333, 333, 2, 2, 192, 0),
     (1, 129, 600, 4, 2, 192, 4),
+    (1, 300, 5000, 4, 2, 128, 4),  # beyond 4096 keys: 192-key tiles where the mode has no 64-key shift
 ]
 
 

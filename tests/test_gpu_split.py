@@ -34,7 +34,7 @@ SHORT_KEYS = 4096  # launches with at most this many keys use 128-key tiles inst
 def tile_keys(fp8, dqk, block64, p_mode, Nk):
     if not fp8:
         return 128 if dqk == 128 else 64
-    long_tiles = dqk == 128 and not block64 and p_mode not in ("lean_block", "exact_block") and Nk > SHORT_KEYS
+    long_tiles = dqk == 128 and p_mode not in ("lean_block", "exact_block") and Nk > SHORT_KEYS
     return 192 if long_tiles else 128
 
 
