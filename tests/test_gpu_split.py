@@ -98,6 +98,7 @@ CASES = [
     ("fp8", 1, 1500, 1500, 2, 2, 128, "block64", "lean"),
     ("fp8", 1, 1500, 1500, 2, 2, 128, "block64", "lean_block"),
     ("fp8", 1, 300, 9000, 4, 1, 128, "head", "lean_tile"),  # short chunk, long prefix
+    ("fp8", 1, 300, 9000, 4, 2, 128, "block64", "lean_tile"),  # block scales on 192-key tiles, split
     ("fp8", 1, 1, 5000, 2, 2, 128, "head", "exact_tile"),  # one query
     ("bf16", 1, 1800, 1800, 2, 1, 128, "head", "lean"),  # 128-key tiles
     ("bf16", 1, 1000, 1000, 2, 2, 192, "head", "lean"),  # 64-key tiles
