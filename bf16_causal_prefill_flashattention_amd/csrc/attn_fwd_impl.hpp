@@ -1169,7 +1169,8 @@ template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bo
 __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>(), NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-  __shared__ uint32_t ebuf[BS ? (C::BN == 192 ? 2 : 1) * (kBlock64MaxKeys / C::BN + 1) : 1];
+  // (block scales: words for tiles 0 .. T, T = ceil(keys / BN) at most)
+  __shared__ uint32_t ebuf[BS ? (C::BN == 192 ? 2 : 1) * ((kBlock64MaxKeys + C::BN - 1) / C::BN + 1) : 1];
   const int nqt = (p.Nq + 32 * NW - 1) / (32 * NW);  // work items of 32 queries per wave
   const int nbh = p.B * p.Hq;
   const int G = gridDim.x, wg = blockIdx.x;
