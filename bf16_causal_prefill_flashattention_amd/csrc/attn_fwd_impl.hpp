@@ -121,12 +121,11 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kBM = kQueryTile;  // queries per workgroup (8 waves x 32)
 
 // Keys per tile.  A phase carries a roughly fixed cost (barriers, the first
-// operand reads), so larger tiles amortise it.  FP8 at d = 128 with one scale
-// per head streams 192-key tiles (128 in launches of at most kShortKeys keys,
-// whose last query tiles would waste more of a final 192-key tile); 128 where
-// the per-64-key probability shift
-// (its four max chains) or the per-64-position scale exponents (one word per
-// 128-key tile) assume it, and at d = 192 (192-byte K rows do not split 192
+// operand reads), so larger tiles amortise it.  FP8 at d = 128 streams
+// 192-key tiles, with one scale per head or per 64 positions (128 in launches
+// of at most kShortKeys keys, whose last query tiles would waste more of a
+// final 192-key tile); 128 where the per-64-key probability shift (its four
+// max chains) assumes it, and at d = 192 (192-byte K rows do not split 192
 // keys into whole 1 KB load blocks per wave).  BF16 at d = 128 streams 128
 // keys (its two 32 KB buffers of K and of V fill 128 KB of LDS, and 192 would
 // not fit it); BF16 at d = 192 stays at 64 (its 384-byte K rows would not
