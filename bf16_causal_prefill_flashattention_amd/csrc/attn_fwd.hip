@@ -178,6 +178,7 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
   const long long tiles = attn_fwd_tiles(p.B, p.Hq, p.Nq);
   AttnParams lp = p;
   lp.solo = 0;
+  lp.snake = 0;
   dim3 grid;
   int first_qt = 0;
   if (p.split_tiles > 0) {
@@ -201,6 +202,15 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
       // as many workgroups as CUs, or one per tile when the tiles do not fill
       // the CUs (the kernel derives the same choice from gridDim)
       grid = dim3(tiles <= cus ? (int)tiles : (int)std::min<long long>(units, cus));
+      // Pairs of equal cost balance the CUs when they split evenly over them;
+      // otherwise (e.g. 384 pairs on 256 CUs) the last round of pairs runs on
+      // part of the CUs only, and dealing single tiles in snake order of cost
+      // over all CUs evens the load out.
+      // (per-head scales and BF16; tile positions stay in int)
+      if (units > cus && units % cus != 0 && !p.block64 && tiles < (1LL << 30)) {
+        lp.snake = 1;
+        grid = dim3(cus);
+      }
     }
   }
   if (dtype == 0) e = launch_attn_bf16(lp, d_qk, grid, stream);

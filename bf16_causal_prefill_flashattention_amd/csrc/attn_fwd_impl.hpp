@@ -1163,8 +1163,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& p, uint8_t* smem, ui
 // equal cost started together, every workgroup of an XCD then reads key tile t
 // at about the same moment in both halves (time t in the heavy half, a constant
 // minus t in the light half), so the workgroups stream two shared fronts of K/V
-// tiles instead of one stream each.
-template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT, int NW>
+// tiles instead of one stream each.  SNAKE: the tiles dealt one by one in snake
+// order of cost instead, for launches whose pairs do not split evenly over the
+// workgroups.
+template <int DQK, int DV, bool FP8, bool BS, int PSH, bool LEAN, bool SPLIT, bool SHORT, int NW, bool SNAKE = false>
 __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
   using C = Cfg<FP8, DQK, DV, tile_keys<FP8, DQK, BS, PSH, SHORT>(), NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
@@ -1189,6 +1191,20 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
     const bool multi = (qtile_key_tiles(qt, p.Nq, p.Nk, C::BN) + L - 1) / L > 1;
     attn_item<DQK, DV, FP8, BS, PSH, LEAN, true, SHORT, NW>(p, smem, ebuf, bh, qt, false, r * L, r * L + L,
                                                  multi ? bh * per_bh + j : -1);
+  } else if constexpr (SNAKE) {
+    // The tiles sorted by cost, heaviest first (position pos: query tile
+    // nqt - 1 - pos / nbh of (batch, head) pos % nbh), dealt in snake order:
+    // round r gives workgroup wg position r * G + wg (r even) or
+    // r * G + G - 1 - wg (r odd).  Used where heavy/light pairs would not
+    // split evenly over the workgroups.  The odd rounds walk their keys
+    // downward, as the lighter tile of a pair does.
+    const int ntiles = nbh * nqt;
+    for (int r = 0; r * G < ntiles; ++r) {
+      const int pos = r * G + ((r & 1) ? G - 1 - wg : wg);
+      if (pos < ntiles)
+        attn_item<DQK, DV, FP8, BS, PSH, LEAN, false, SHORT, NW>(p, smem, ebuf, pos % nbh, nqt - 1 - pos / nbh,
+                                                                (r & 1) != 0, 0, 0, -1);
+    }
   } else {
     const bool single = (long long)nbh * nqt <= G;  // one tile per unit
     const int per_bh = single ? nqt : (nqt + 1) / 2;  // units per (batch, head)
@@ -1216,26 +1232,33 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_fwd_kernel(AttnParams p) {
 
 // Launch one variant (d_v = 128) on `grid` persistent workgroups: the split
 // instantiation when the launch splits its keys, the 4-wave one when the
-// launch runs 128-query items (p.solo), and the short-sequence tile size where
-// it differs (kShortKeys).
+// launch runs 128-query items (p.solo), the snake-order one when its pairs do
+// not split evenly over the workgroups (p.snake), and the short-sequence tile
+// size where it differs (kShortKeys).
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN, bool SHORT>
 hipError_t launch_attn_tiles(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.split_tiles > 0)
+  if (p.split_tiles > 0) {
     hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, true, SHORT, 8>), grid, dim3(512), 0, stream, p);
-  else if constexpr (tile_keys<FP8, DQK, BS, PSH, SHORT>() <= 128) {
+  } else if (p.snake) {
+    // (per-head scales only: the block-scaled kernels keep the pairs, as their
+    // snake-order build reloads spilled scalars in its main loop)
+    if constexpr (!BS)
+      hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 8, true>), grid, dim3(512), 0,
+                         stream, p);
+    else
+      return hipErrorInvalidValue;
+  } else if (p.solo) {
     // (the 4-wave mode exists for tiles of at most 128 keys; the host picks it
     // only for those)
-    if (p.solo)
+    if constexpr (tile_keys<FP8, DQK, BS, PSH, SHORT>() <= 128)
       hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 4>), grid, dim3(256), 0, stream,
                          p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 8>), grid, dim3(512), 0,
-                         stream, p);
-  } else if (p.solo)
-    return hipErrorInvalidValue;
-  else
+      return hipErrorInvalidValue;
+  } else {
     hipLaunchKernelGGL((attn_fwd_kernel<DQK, 128, FP8, BS, PSH, LEAN, false, SHORT, 8>), grid, dim3(512), 0, stream,
                        p);
+  }
   return hipGetLastError();
 }
 template <int DQK, bool FP8, bool BS, int PSH, bool LEAN>

@@ -41,6 +41,10 @@ struct AttnParams {
   int split_units;
   // set by launch_attn_fwd: 1 runs 128-query items on 4-wave workgroups (see kSoloQueryTile)
   int solo;
+  // set by launch_attn_fwd: 1 deals the query tiles to the persistent
+  // workgroups in snake order of cost instead of as heavy/light pairs (when
+  // the pairs do not split evenly over the workgroups)
+  int snake;
   float* ws_o;
   float* ws_lse;
 };

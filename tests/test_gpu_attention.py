@@ -122,6 +122,53 @@ def test_paired_persistent_full_compare(require_gpu, dtype, B, N, Hq, Hkv, dqk):
     assert rel_fro(out, ref) <= TOL[dtype] and err.max() <= TOL[dtype], err
 
 
+def _snake_heads(cus, N, G):
+    """The fewest heads (a multiple of G) whose heavy/light pairs of 256-query
+    tiles outnumber the CUs without splitting evenly over them, the launches
+    dealt in snake order of cost."""
+    pairs = ((N + 255) // 256 + 1) // 2
+    H = G
+    while not (H * pairs > cus and (H * pairs) % cus != 0):
+        H += G
+    return H
+
+
+SNAKE = [
+    # (dtype, N, Hkv, d_qk)
+    ("bf16", 1280, 8, 128),
+    ("fp8", 1280, 8, 128),
+    ("fp8", 1100, 8, 192),
+    ("bf16", 1100, 8, 192),
+]
+
+
+@pytest.mark.parametrize("dtype,N,Hkv,dqk", SNAKE)
+def test_snake_order_full_compare(require_gpu, dtype, N, Hkv, dqk):
+    """Launches whose tile pairs do not split evenly over the CUs deal single
+    tiles in snake order of cost (every odd round walking its keys downward):
+    the whole output against the oracle, and repeated launches bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hq = _snake_heads(cus, N, Hkv)
+    w = Workload("t", dtype, 1, Hq, Hkv, N, dqk, 128, outliers=4, seed=N + Hq)
+    if dtype == "bf16":
+        q, k, v = make_inputs(w)
+        dev = [t.cuda() for t in (q, k, v)]
+        ref = attn_ref(q, k, v)
+    else:
+        q, k, v = make_qkv(w)
+        cq, sq, ck, sk, cv, sv = _fp8_oracle_inputs(q, k, v, False)
+        dev = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (cq, ck, cv, sq, sk, sv)]
+        ref = attn_ref(dequantize_ref(cq, sq), dequantize_ref(ck, sk), dequantize_ref(cv, sv))
+    out = miattn.attn_fwd(*dev)
+    torch.cuda.synchronize()
+    first = out.view(torch.int16).clone()
+    err = per_head_rel_fro(out.cpu(), ref)
+    assert rel_fro(out.cpu(), ref) <= TOL[dtype] and err.max() <= TOL[dtype], err
+    for _ in range(10):
+        miattn.attn_fwd(*dev, out=out)
+        assert torch.equal(out.view(torch.int16), first)
+
+
 # ---------------------------------------------------------------- special cases
 
 
