@@ -203,11 +203,11 @@ hipError_t launch_attn_fwd(const AttnParams& p, int dtype, int d_qk, int d_v, hi
       // the CUs (the kernel derives the same choice from gridDim)
       grid = dim3(tiles <= cus ? (int)tiles : (int)std::min<long long>(units, cus));
       // Pairs of equal cost balance the CUs when they split evenly over them;
-      // otherwise (e.g. 384 pairs on 256 CUs) the last round of pairs runs on
-      // part of the CUs only, and dealing single tiles in snake order of cost
-      // over all CUs evens the load out.
+      // otherwise (e.g. 384 pairs, or 192, on 256 CUs) a round of pairs runs
+      // on part of the CUs only, and dealing single tiles in snake order of
+      // cost over all CUs evens the load out.
       // (per-head scales and BF16; tile positions stay in int)
-      if (units > cus && units % cus != 0 && !p.block64 && tiles < (1LL << 30)) {
+      if (tiles > cus && units % cus != 0 && !p.block64 && tiles < (1LL << 30)) {
         lp.snake = 1;
         grid = dim3(cus);
       }

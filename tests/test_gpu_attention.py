@@ -93,20 +93,27 @@ def test_fp8_small_full_compare(require_gpu, B, N, Hq, Hkv, dqk, outl, hadamard)
 
 
 PAIRED = [
-    # (dtype, B, N, Hq, Hkv, d_qk): more 256-query tiles than CUs, so every
-    # persistent workgroup runs pairs of tiles, the lighter tile of a pair with
-    # its keys walked downward; an odd tile count leaves a middle tile unpaired
-    ("bf16", 1, 1280, 64, 8, 128),
-    ("fp8", 1, 1280, 64, 8, 128),
-    ("fp8", 1, 1100, 64, 16, 192),
-    ("bf16", 2, 1100, 32, 32, 192),
+    # (dtype, B, N, Hkv, d_qk): more 256-query tiles than CUs, in pairs that
+    # split evenly over the CUs (the heads are chosen for that), so every
+    # persistent workgroup runs heavy/light pairs of tiles, the lighter tile of
+    # a pair with its keys walked downward; an odd tile count leaves a middle
+    # tile unpaired
+    ("bf16", 1, 1700, 8, 128),
+    ("fp8", 1, 1700, 8, 128),
+    ("fp8", 1, 1800, 16, 192),
+    ("bf16", 2, 1800, 32, 192),
 ]
 
 
-@pytest.mark.parametrize("dtype,B,N,Hq,Hkv,dqk", PAIRED)
-def test_paired_persistent_full_compare(require_gpu, dtype, B, N, Hq, Hkv, dqk):
+@pytest.mark.parametrize("dtype,B,N,Hkv,dqk", PAIRED)
+def test_paired_persistent_full_compare(require_gpu, dtype, B, N, Hkv, dqk):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert B * Hq * ((N + 255) // 256) > cus, "the case must launch in paired mode"
+    nqt = (N + 255) // 256
+    pairs = (nqt + 1) // 2
+    if cus % (B * pairs) or (cus // (B * pairs)) % Hkv:
+        pytest.skip("no head count splits these pairs evenly over this device's CUs")
+    Hq = cus // (B * pairs)
+    assert B * Hq * nqt > cus and (B * Hq * pairs) % cus == 0, "the case must launch in paired mode"
     w = Workload("t", dtype, B, Hq, Hkv, N, dqk, 128, outliers=4, seed=N + Hq + B)
     if dtype == "bf16":
         out, (q, k, v) = _bf16_case(w)

@@ -155,13 +155,16 @@ def test_default_fp8_path_keeps_far_key_blocks(require_gpu):
     _check_lse("fp8", lse.cpu().numpy().astype(np.float64), ref_lse, ref_in)
 
 
+@pytest.mark.parametrize("N", [1700, 1280])
 @pytest.mark.parametrize("mode", ["lean_tile", "exact", "exact_tile"])
-def test_modes_bitwise_deterministic_in_paired_mode(require_gpu, mode):
-    """100 launches of a paired-mode shape (more 256-query tiles than CUs)."""
-    w = Workload("t", "fp8", 1, 64, 8, 1280, 128, 128, outliers=4, seed=41)
+def test_modes_bitwise_deterministic_in_paired_mode(require_gpu, mode, N):
+    """100 launches of persistent-mode shapes (more 256-query tiles than CUs):
+    at 1700 tokens 64 heads make 256 heavy/light pairs, at 1280 tokens 192,
+    which a 256-CU device deals as single tiles in snake order instead."""
+    w = Workload("t", "fp8", 1, 64, 8, N, 128, 128, outliers=4, seed=41)
     q, k, v = make_qkv(w)
     dev, _ = _quantized(q, k, v, "head")
-    out = torch.empty((1, 1280, 64, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, N, 64, 128), dtype=torch.bfloat16, device="cuda")
     miattn.attn_fwd_fp8(*dev, out=out, with_lse=False, p_mode=mode)
     torch.cuda.synchronize()
     first = out.view(torch.int16).clone()
